@@ -1,0 +1,291 @@
+// Grouped-query decode attention over the paged KV cache (split-K), gfx950.
+//
+// One new token per sequence at position len attends to all len + 1 keys of
+// its sequence (the cached ones plus its own, appended by the QKV epilogue
+// before this kernel runs): "Chapter 10: the modern LLaMA architecture",
+// section 7 (q_len = 1, k_len = past_len + 1).  Query head h reads KV head
+// g = h / (H/G) (section 6).  The step is bound by HBM: every key and value
+// of the batch is read once per KV group, shared by the R = H/G query heads.
+//
+// Split kernel: a workgroup (4 waves) takes one (sequence, group, chunk of
+// 1024 keys); each wave walks 32-key steps (two 16-key cache blocks) and
+// runs both products on 16x16 MFMAs with the R heads as the 16 columns:
+//   S^T [16 keys x heads] = K_block [16 x D] * Q^T   (K loaded straight from HBM)
+//   O^T [D x heads]      += V_block^T [D x 32 keys] * P^T
+// V is kept transposed per block in the cache, so the A operand of the second
+// product is a plain 8/16-byte load.  The online softmax state (running max
+// and sum per head) lives in the lanes; the four waves are merged through LDS
+// and the chunk's (max, sum, unnormalised output) go to a partial buffer.
+// Combine kernel: per (sequence, head), a log-sum-exp merge of the chunks.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+namespace {
+
+constexpr int kChunkKeys = 1024;
+
+template <typename T, int D_>
+struct DCfg {
+  static constexpr int D = D_;
+  static constexpr int CH = Chunk<T>::N;
+  static constexpr int NQK = D / (4 * CH);  // 16x16 MFMA chunk-steps over D
+  static constexpr int NDB = D / 16;        // 16-row blocks of O^T
+};
+
+template <typename T>
+struct VPiece;  // 4 consecutive keys of one V^T row
+template <> struct VPiece<bf16> { typedef u32x2 type; };
+template <> struct VPiece<float> { typedef u32x4 type; };
+
+// Zero the elements e >= n of a 4-key piece (bf16: two words, fp32: four words).
+DEVI u32x2 keep_first(u32x2 w, int n) {
+  w[0] = n >= 2 ? w[0] : (n == 1 ? (w[0] & 0xFFFFu) : 0u);
+  w[1] = n >= 4 ? w[1] : (n == 3 ? (w[1] & 0xFFFFu) : 0u);
+  return w;
+}
+DEVI u32x4 keep_first(u32x4 w, int n) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = e < n ? w[e] : 0u;
+  return w;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restrict__ q, float* __restrict__ part,
+                                                                int max_splits, int H, CacheView cache,
+                                                                BatchView batch) {
+  using C = DCfg<T, D>;
+  using vec = typename Chunk<T>::vec;
+  using piece = typename VPiece<T>::type;
+  __shared__ float sm[4][16][D + 2];
+
+  const int G = cache.G;
+  const int R = H / G;
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const int split = blockIdx.y;
+  const int seq = batch.desc[2 * b];
+  const int kv_len = batch.desc[2 * b + 1] + 1;
+  const int k_begin = split * kChunkKeys;
+  if (k_begin >= kv_len) return;
+  const int k_end = min(kv_len, k_begin + kChunkKeys);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int HD = H * D;
+
+  // Q^T fragments: column c16 = query head g*R + c16 (zero for c16 >= R)
+  vec qf[C::NQK];
+  {
+    const T* qp = q + (size_t)b * HD + (size_t)(g * R + c16) * D;
+#pragma unroll
+    for (int s = 0; s < C::NQK; ++s)
+      qf[s] = c16 < R ? load_chunk<T>(qp + (4 * s + g4) * C::CH) : zero_chunk<T>();
+  }
+
+  const T* kpool = reinterpret_cast<const T*>(cache.k_pool);
+  const T* vpool = reinterpret_cast<const T*>(cache.v_pool);
+  const int32_t* btab = cache.block_table + (size_t)seq * cache.max_blocks;
+
+  const float scale = 1.4426950408889634f / sqrtf((float)D);
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[C::NDB];
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int key0 = k_begin + 32 * wave; key0 < k_end; key0 += 128) {
+    vec kf[2][C::NQK];
+    piece vf[2][C::NDB];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kb0 = key0 + 16 * u;
+      if (kb0 < kv_len) {
+        const size_t blk = (size_t)btab[kb0 >> 4];
+        const T* kp = kpool + ((blk * G + g) * 16 + c16) * D;
+#pragma unroll
+        for (int s = 0; s < C::NQK; ++s) kf[u][s] = load_chunk<T>(kp + (4 * s + g4) * C::CH);
+        const T* vp = vpool + (blk * G + g) * D * 16;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db)
+          vf[u][db] = *reinterpret_cast<const piece*>(vp + (16 * db + c16) * 16 + 4 * g4);
+        if (kb0 + 16 > kv_len) {  // keys past the end may hold stale data: zero their values
+          const int nvalid = kv_len - (kb0 + 4 * g4);
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) vf[u][db] = keep_first(vf[u][db], nvalid);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < C::NQK; ++s) kf[u][s] = zero_chunk<T>();
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) vf[u][db] = piece{};
+      }
+    }
+
+    // scores: lane holds head c16, keys key0 + 16u + 4*g4 + i
+    f32x4 sc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < C::NQK; ++s) sc[u] = mfma16_chunk(sc[u], kf[u][s], qf[s]);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = key0 + 16 * u + 4 * g4 + i;
+        const float sv = key < kv_len ? sc[u][i] * scale : -INFINITY;
+        sc[u][i] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = exp2f(sc[u][i] - m_new);
+        sc[u][i] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+
+    // O^T += V^T P^T: element e < 4 of a lane's operand is key 4*g4+e of the
+    // first block, e >= 4 the same key of the second block.
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 pb = {from_f32<bf16>(sc[0][0]), from_f32<bf16>(sc[0][1]), from_f32<bf16>(sc[0][2]),
+                         from_f32<bf16>(sc[0][3]), from_f32<bf16>(sc[1][0]), from_f32<bf16>(sc[1][1]),
+                         from_f32<bf16>(sc[1][2]), from_f32<bf16>(sc[1][3])};
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        const u32x2 lo = __builtin_bit_cast(u32x2, vf[0][db]);
+        const u32x2 hi = __builtin_bit_cast(u32x2, vf[1][db]);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        o[db] = mfma16_chunk(o[db], a, pb);
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        o[db] = mfma16_chunk(o[db], __builtin_bit_cast(f32x4, vf[0][db]), sc[0]);
+        o[db] = mfma16_chunk(o[db], __builtin_bit_cast(f32x4, vf[1][db]), sc[1]);
+      }
+    }
+  }
+
+  // ---- merge the four waves ----
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sm[wave][c16][2 + 16 * db + 4 * g4 + i] = o[db][i];
+  if (g4 == 0) {
+    sm[wave][c16][0] = m_run;
+    sm[wave][c16][1] = l_run;
+  }
+  __syncthreads();
+  // 256 threads: head hh = tid / 16 (16 heads), 16 threads per head over D + 2 values
+  const int hh = tid >> 4, sub = tid & 15;
+  if (hh >= R) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][hh][0]);
+  float f[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) f[w] = exp2f(sm[w][hh][0] - M);  // waves without keys: exp2(-inf) = 0
+  float* dst = part + (((size_t)b * H + g * R + hh) * max_splits + split) * (D + 2);
+  for (int x = sub; x < D + 2; x += 16) {
+    float v;
+    if (x == 0) {
+      v = M;
+    } else {
+      v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v += f[w] * sm[w][hh][x];
+    }
+    dst[x] = v;
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* __restrict__ part, T* __restrict__ attn,
+                                                                  int max_splits, int H, BatchView batch) {
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (bh >= batch.batch * H) return;
+  const int b = bh / H, h = bh % H;
+  const int kv_len = batch.desc[2 * b + 1] + 1;
+  const int ns = (kv_len + kChunkKeys - 1) / kChunkKeys;
+  const float* p = part + (size_t)bh * max_splits * (D + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, p[s * (D + 2)]);
+  float L = 0.f;
+  float acc[D / 64];
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float* ps = p + s * (D + 2);
+    const float f = exp2f(ps[0] - M);
+    L += f * ps[1];
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) acc[e] += f * ps[2 + lane + 64 * e];
+  }
+  const float inv = 1.f / L;
+  T* out = attn + (size_t)b * H * D + (size_t)h * D;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = from_f32<T>(acc[e] * inv);
+}
+
+template <typename T, int D>
+hipError_t launch_split(const void* q, float* part, int max_splits, int H, const CacheView& c, const BatchView& b,
+                        hipStream_t s) {
+  dim3 grid(c.G * b.batch, max_splits);
+  attn_decode_split_kernel<T, D><<<grid, 256, 0, s>>>(reinterpret_cast<const T*>(q), part, max_splits, H, c, b);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_combine(const float* part, void* attn, int max_splits, int H, const BatchView& b, hipStream_t s) {
+  const int nbh = b.batch * H;
+  attn_decode_combine_kernel<T, D><<<(nbh + 3) / 4, 256, 0, s>>>(part, reinterpret_cast<T*>(attn), max_splits, H, b);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int decode_split_keys() { return kChunkKeys; }
+
+hipError_t launch_attn_decode(DType t, const void* q, float* partial, int max_splits, int H, const CacheView& c,
+                              const BatchView& b, hipStream_t s) {
+  if (H % c.G != 0 || H / c.G > 16) return hipErrorInvalidValue;
+  if (t == DType::BF16) {
+    if (c.D == 128) return launch_split<bf16, 128>(q, partial, max_splits, H, c, b, s);
+    if (c.D == 64) return launch_split<bf16, 64>(q, partial, max_splits, H, c, b, s);
+  } else {
+    if (c.D == 128) return launch_split<float, 128>(q, partial, max_splits, H, c, b, s);
+    if (c.D == 64) return launch_split<float, 64>(q, partial, max_splits, H, c, b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_attn_decode_combine(DType t, const float* partial, void* attn, int max_splits, int H, int D,
+                                      const BatchView& b, hipStream_t s) {
+  if (t == DType::BF16) {
+    if (D == 128) return launch_combine<bf16, 128>(partial, attn, max_splits, H, b, s);
+    if (D == 64) return launch_combine<bf16, 64>(partial, attn, max_splits, H, b, s);
+  } else {
+    if (D == 128) return launch_combine<float, 128>(partial, attn, max_splits, H, b, s);
+    if (D == 64) return launch_combine<float, 64>(partial, attn, max_splits, H, b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace llk

@@ -1,0 +1,97 @@
+// Device-side building blocks shared by the gfx950 kernels of the decoder layer:
+// element types, 16-byte chunk loads, fp32 <-> bf16 conversion, and MFMA wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define DEVI __device__ __forceinline__
+
+// ---------------------------------------------------------------------------
+// scalar conversions (fp32 -> bf16 is round-to-nearest-even on gfx950)
+// ---------------------------------------------------------------------------
+DEVI float to_f32(float v) { return v; }
+DEVI float to_f32(bf16 v) { return static_cast<float>(v); }
+template <typename T> DEVI T from_f32(float v);
+template <> DEVI float from_f32<float>(float v) { return v; }
+template <> DEVI bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
+
+// ---------------------------------------------------------------------------
+// 16-byte chunks: 8 bf16 or 4 fp32 elements
+// ---------------------------------------------------------------------------
+template <typename T> struct Chunk;
+template <> struct Chunk<bf16> {
+  static constexpr int N = 8;
+  typedef bf16x8 vec;
+};
+template <> struct Chunk<float> {
+  static constexpr int N = 4;
+  typedef f32x4 vec;
+};
+
+template <typename T>
+DEVI typename Chunk<T>::vec load_chunk(const T* p) {
+  return *reinterpret_cast<const typename Chunk<T>::vec*>(p);
+}
+template <typename T>
+DEVI void store_chunk(T* p, typename Chunk<T>::vec v) {
+  *reinterpret_cast<typename Chunk<T>::vec*>(p) = v;
+}
+template <typename T>
+DEVI typename Chunk<T>::vec zero_chunk() {
+  typename Chunk<T>::vec z;
+  for (int i = 0; i < Chunk<T>::N; ++i) z[i] = from_f32<T>(0.f);
+  return z;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16: one 16-byte chunk per lane of each operand.
+//   A: lane l holds row (l & 15); B: lane l holds column (l & 15); lane group
+//   g = l >> 4 supplies k-elements from its chunk.  Any assignment of k to
+//   (lane group, element) works as long as A and B use the same one.
+//   C/D: lane l holds column (l & 15), rows 4 * (l >> 4) + {0,1,2,3}.
+// bf16: one v_mfma_f32_16x16x32_bf16.  fp32: four v_mfma_f32_16x16x4_f32.
+// ---------------------------------------------------------------------------
+DEVI f32x4 mfma16_chunk(f32x4 c, bf16x8 a, bf16x8 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+DEVI f32x4 mfma16_chunk(f32x4 c, f32x4 a, f32x4 b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+  return c;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32: A lane l holds row (l & 31), B lane l holds column (l & 31),
+// lane group h = l >> 5 supplies k-elements.  C/D (16 floats): lane l holds
+// column (l & 31), rows 8 * (i / 4) + 4 * h + (i % 4) for register i.
+// bf16: one v_mfma_f32_32x32x16_bf16 per chunk; fp32: four v_mfma_f32_32x32x2_f32.
+// ---------------------------------------------------------------------------
+DEVI f32x16 mfma32_chunk(f32x16 c, bf16x8 a, bf16x8 b) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+DEVI f32x16 mfma32_chunk(f32x16 c, f32x4 a, f32x4 b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], b[0], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], b[1], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], b[2], c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], b[3], c, 0, 0, 0);
+  return c;
+}
+
+DEVI int lane_id() { return __lane_id(); }
+
+// Exchange with lane l ^ m within a wave (m < 64).
+DEVI float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+template <typename T> DEVI T ceil_div(T a, T b) { return (a + b - 1) / b; }

@@ -1,0 +1,112 @@
+// Internal launch interface between the host runtime (llama_layer.cpp) and the
+// gfx950 kernels.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace llk {
+
+enum class DType : int { F32 = 0, BF16 = 1 };
+
+inline size_t dsize(DType t) { return t == DType::F32 ? 4 : 2; }
+
+// Per-call description of the batch, resident in device memory:
+// desc[2*b] = seq_id, desc[2*b+1] = first new position of sequence b.
+struct BatchView {
+  const int32_t* desc;
+  int batch;
+  int seq_len;  // new tokens per sequence (1 for decode)
+};
+
+// Paged KV cache as the kernels see it.  K and V pools are
+// [num_blocks][G][16][D]; the block table is [max_seqs][max_blocks].
+struct CacheView {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* block_table;
+  int max_blocks;
+  int G, D;
+};
+
+enum class Epi : int { QKV = 0, RESID_H = 1, SWIGLU = 2, RESID_OUT = 3 };
+
+struct GemmArgs {
+  const void* W;  // packed weights [N][K] (features x K), K-contiguous
+  const void* X;  // activations [M][ldx], K-contiguous
+  int M, N, K, ldx;
+  Epi epi;
+  const float* rowscale;  // QKV / SWIGLU: per-token RMSNorm scale
+  // QKV epilogue
+  void* q_out;  // [M][H*D]
+  CacheView cache;
+  BatchView batch;
+  const float* rope_cos;  // [max_position][D/2]
+  const float* rope_sin;
+  int H;
+  // residual / output epilogues
+  const void* resid;  // RESID_H: x [M][N] (layer dtype); RESID_OUT: h [M][N] fp32
+  void* out;          // RESID_H: h fp32; SWIGLU: s [M][ldo]; RESID_OUT: out
+  int ldo;
+  DType out_dtype;    // RESID_OUT only
+};
+
+// Tile shape chosen by the host for a GEMM.
+enum class GemmTile : int { LARGE = 0, SMALL = 1 };
+int gemm_tile_n(GemmTile t);  // features per workgroup tile
+
+hipError_t launch_gemm(DType t, GemmTile tile, const GemmArgs& a, hipStream_t s);
+
+// RMSNorm row scale r[t] = rsqrt(mean(x[t]^2) + eps) of x [M][d] (layer dtype).
+hipError_t launch_rms_rowscale(DType t, const void* x, float* r, int M, int d, float eps,
+                               hipStream_t s);
+// Second norm: r2[t] from h [M][d] fp32, plus hb = h converted to the layer dtype.
+hipError_t launch_rms_convert(DType t, const float* h, void* hb, float* r, int M, int d,
+                              float eps, hipStream_t s);
+
+// Causal GQA prefill attention: q [B*S][H*D] -> attn [B*S][H*D], keys from the cache.
+hipError_t launch_attn_prefill(DType t, const void* q, void* attn, int H, const CacheView& c,
+                               const BatchView& b, hipStream_t s);
+
+// Split-K paged decode attention.  partial: [B][H][max_splits][D + 2] fp32
+// holding (running max, sum, unnormalised output) per key chunk; the combine
+// kernel merges the chunks into attn [B][H*D].
+int decode_split_keys();
+hipError_t launch_attn_decode(DType t, const void* q, float* partial, int max_splits, int H,
+                              const CacheView& c, const BatchView& b, hipStream_t s);
+hipError_t launch_attn_decode_combine(DType t, const float* partial, void* attn, int max_splits,
+                                      int H, int D, const BatchView& b, hipStream_t s);
+
+// Weight packing.  dst[r][c] = src[r][c] * (gamma ? gamma[c] : 1) for r < rows,
+// c < cols; padded columns up to ldd and padded rows up to rows_pad are zero.
+// Row r of the source lands at dst row (r * row_mul + row_add).
+hipError_t launch_pack(DType t, const void* src, const void* gamma, void* dst, int rows,
+                       int cols, int ldd, int row_mul, int row_add, hipStream_t s);
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s);
+
+// Small host -> device updates carried in kernel arguments: base[idx[i]] = val[i].
+constexpr int kUploadMax = 240;
+struct Upload {
+  int32_t* base;
+  int n;
+  int32_t idx[kUploadMax];
+  int32_t val[kUploadMax];
+};
+hipError_t launch_upload(const Upload& u, hipStream_t s);
+
+// Host -> device copy on a stream, and a stream wait (set-up calls only).
+hipError_t copy_to_device(void* dst, const void* src, size_t bytes, hipStream_t s);
+hipError_t stream_sync(hipStream_t s);
+
+// Events for per-kernel timing (opaque hipEvent_t handles).
+hipError_t event_create(void** ev);
+hipError_t event_destroy(void* ev);
+hipError_t event_record(void* ev, hipStream_t s);
+hipError_t event_elapsed_ms(float* ms, void* start, void* stop);  // waits for `stop`
+
+// Contiguous [n][G][D] <-> paged cache for positions start.. of one sequence.
+hipError_t launch_kv_copy(DType t, const CacheView& c, int seq, int start, int n, void* k,
+                          void* v, bool to_cache, hipStream_t s);
+
+}  // namespace llk

@@ -1,0 +1,739 @@
+// Host runtime of the decoder-layer library: C ABI, argument validation, the
+// paged-KV block manager, weight packing, workspace carving and the launch
+// sequence of one prefill or decode call.
+//
+// The launch sequence follows the layer as the pages state it ("LLaMA3
+// Block: from parts to engine", 4.2; "Chapter 10: the modern LLaMA
+// architecture", section 9):
+//   r1 = rowscale(x)                                  RMSNorm_1 statistics
+//   [q | k | v] = r1 * x W'qkv^T, RoPE(q, k), k/v -> cache    (W' = W diag(gamma_1))
+//   attn = causal GQA attention(q, cache)             prefill: flash; decode: split-K
+//   h = x + attn Wo^T                                  fp32 residual stream
+//   r2 = rowscale(h), hb = h in the layer dtype       RMSNorm_2 statistics
+//   s = SiLU(r2 * hb W'g^T) * (r2 * hb W'u^T)          (W' = W diag(gamma_2))
+//   out = h + s Wd^T
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/llama_layer.h"
+#include "kernels.h"
+
+using llk::DType;
+
+namespace {
+
+constexpr int kBlock = 16;
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Shape {
+  int d, I, I_pad, H, G, D, HD, KD, NQKV, NQKV_pad, max_pos;
+  DType dt;
+  size_t es;
+};
+
+llama_status check_config(const llama_layer_config* c, Shape* s) {
+  if (!c) return LLAMA_ERR_INVALID_ARG;
+  if (c->dtype != LLAMA_DTYPE_F32 && c->dtype != LLAMA_DTYPE_BF16) return LLAMA_ERR_DTYPE;
+  if (c->hidden_size <= 0 || c->intermediate_size <= 0 || c->num_attention_heads <= 0 ||
+      c->num_key_value_heads <= 0 || c->max_position <= 0)
+    return LLAMA_ERR_INVALID_ARG;
+  if (!(c->rms_norm_eps > 0.f) || !std::isfinite(c->rms_norm_eps) || !(c->rope_theta > 1.f) ||
+      !std::isfinite(c->rope_theta))
+    return LLAMA_ERR_INVALID_ARG;
+  // "From Transformer to the LLaMA series", section 8: heads must split evenly
+  if (c->num_attention_heads % c->num_key_value_heads != 0) return LLAMA_ERR_SHAPE;
+  if (c->hidden_size % c->num_attention_heads != 0) return LLAMA_ERR_SHAPE;
+  const int D = c->hidden_size / c->num_attention_heads;
+  if (D % 2 != 0) return LLAMA_ERR_SHAPE;  // RoPE pairs need an even head_dim ("Chapter 10", section 3)
+  if (D != 64 && D != 128) return LLAMA_ERR_UNSUPPORTED;
+  const int R = c->num_attention_heads / c->num_key_value_heads;
+  if (R > 16 || (R & (R - 1)) != 0) return LLAMA_ERR_UNSUPPORTED;
+  if (c->hidden_size % 64 != 0 || c->intermediate_size % 8 != 0) return LLAMA_ERR_SHAPE;
+  if ((int64_t)c->hidden_size > (1 << 16) || (int64_t)c->intermediate_size > (1 << 18) ||
+      c->max_position > (1 << 22))
+    return LLAMA_ERR_SHAPE;
+  s->d = c->hidden_size;
+  s->I = c->intermediate_size;
+  s->I_pad = (c->intermediate_size + 127) / 128 * 128;
+  s->H = c->num_attention_heads;
+  s->G = c->num_key_value_heads;
+  s->D = D;
+  s->HD = s->H * D;
+  s->KD = s->G * D;
+  s->NQKV = s->HD + 2 * s->KD;
+  s->NQKV_pad = (s->NQKV + 255) / 256 * 256;
+  s->max_pos = c->max_position;
+  s->dt = c->dtype == LLAMA_DTYPE_BF16 ? DType::BF16 : DType::F32;
+  s->es = llk::dsize(s->dt);
+  return LLAMA_OK;
+}
+
+struct PackedLayout {
+  size_t qkv, o, gu, down, cos, sin, total;
+};
+
+PackedLayout packed_layout(const Shape& s) {
+  PackedLayout p;
+  size_t off = 0;
+  p.qkv = off;
+  off = align256(off + (size_t)s.NQKV_pad * s.d * s.es);
+  p.o = off;
+  off = align256(off + (size_t)s.d * s.HD * s.es);
+  p.gu = off;
+  off = align256(off + (size_t)2 * s.I_pad * s.d * s.es);
+  p.down = off;
+  off = align256(off + (size_t)s.d * s.I_pad * s.es);
+  p.cos = off;
+  off = align256(off + (size_t)s.max_pos * (s.D / 2) * sizeof(float));
+  p.sin = off;
+  off = align256(off + (size_t)s.max_pos * (s.D / 2) * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+int max_splits_for(const Shape& s) { return (s.max_pos + llk::decode_split_keys() - 1) / llk::decode_split_keys(); }
+
+struct WsLayout {
+  size_t desc, r1, r2, q, attn, h, hb, s, part, total;
+};
+
+WsLayout ws_layout(const Shape& sh, size_t T, size_t B) {
+  WsLayout w;
+  size_t off = 0;
+  w.desc = off;
+  off = align256(off + B * 2 * sizeof(int32_t));
+  w.r1 = off;
+  off = align256(off + T * sizeof(float));
+  w.r2 = off;
+  off = align256(off + T * sizeof(float));
+  w.q = off;
+  off = align256(off + T * sh.HD * sh.es);
+  w.attn = off;
+  off = align256(off + T * sh.HD * sh.es);
+  w.h = off;
+  off = align256(off + T * sh.d * sizeof(float));
+  w.hb = off;
+  off = align256(off + T * sh.d * sh.es);
+  w.s = off;
+  off = align256(off + T * sh.I_pad * sh.es);
+  w.part = off;
+  off = align256(off + B * sh.H * (size_t)max_splits_for(sh) * (sh.D + 2) * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+bool trace_on() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = std::getenv("LLAMA_LAYER_TRACE");
+    v = (e && *e && *e != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+#define HIP_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t _e = (expr);                                                             \
+    if (_e != hipSuccess) {                                                             \
+      if (trace_on()) std::fprintf(stderr, "[llama_layer] %s -> %s\n", #expr, hipGetErrorString(_e)); \
+      return LLAMA_ERR_HIP;                                                             \
+    }                                                                                   \
+  } while (0)
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// handles
+// ---------------------------------------------------------------------------
+
+namespace {
+enum Kern { K_RMS1, K_QKV, K_ATTN_PREFILL, K_ATTN_DECODE, K_ATTN_COMBINE, K_OPROJ, K_RMS2, K_GATEUP, K_DOWN, K_COUNT };
+const char* const kKernNames[K_COUNT] = {"rms_rowscale",   "gemm_qkv_rope",     "attn_prefill",
+                                         "attn_decode_split", "attn_decode_combine", "gemm_o_resid",
+                                         "rms_convert",    "gemm_gate_up_swiglu", "gemm_down_resid"};
+struct Pending {
+  int kind;
+  void* start;
+  void* stop;
+};
+}  // namespace
+
+struct llama_layer {
+  llama_layer_config cfg;
+  Shape s;
+  PackedLayout pl;
+  char* packed;
+  // per-kernel timing
+  bool profiling = false;
+  std::vector<void*> free_events;
+  std::vector<Pending> pending;
+  int launches[K_COUNT] = {};
+  double total_ms[K_COUNT] = {};
+};
+
+namespace {
+
+void drop_events(llama_layer* L) {
+  for (auto& p : L->pending) {
+    (void)llk::event_destroy(p.start);
+    (void)llk::event_destroy(p.stop);
+  }
+  L->pending.clear();
+  for (void* e : L->free_events) (void)llk::event_destroy(e);
+  L->free_events.clear();
+}
+
+hipError_t take_event(llama_layer* L, void** ev) {
+  if (!L->free_events.empty()) {
+    *ev = L->free_events.back();
+    L->free_events.pop_back();
+    return hipSuccess;
+  }
+  return llk::event_create(ev);
+}
+
+// Launch `fn` on stream s, bracketed by timing events when profiling.
+template <typename F>
+hipError_t timed(llama_layer* L, int kind, hipStream_t s, F&& fn) {
+  if (!L->profiling) return fn();
+  void *a = nullptr, *b = nullptr;
+  hipError_t e = take_event(L, &a);
+  if (e == hipSuccess) e = take_event(L, &b);
+  if (e == hipSuccess) e = llk::event_record(a, s);
+  if (e != hipSuccess) return e;
+  e = fn();
+  if (e != hipSuccess) return e;
+  e = llk::event_record(b, s);
+  if (e != hipSuccess) return e;
+  L->pending.push_back({kind, a, b});
+  return hipSuccess;
+}
+
+}  // namespace
+
+struct SeqState {
+  bool open = false;
+  int len = 0;
+  std::vector<int32_t> blocks;
+};
+
+struct llama_kv_cache {
+  Shape s;
+  int num_blocks, max_seqs, max_blocks;
+  void* k_pool;
+  void* v_pool;
+  int32_t* table;
+  std::vector<int32_t> free_blocks;  // handed out from the back
+  std::vector<SeqState> seqs;
+};
+
+namespace {
+
+size_t pool_bytes(const Shape& s, int num_blocks) { return (size_t)num_blocks * s.G * kBlock * s.D * s.es; }
+
+struct CacheLayout {
+  size_t k, v, table, total;
+};
+CacheLayout cache_layout(const Shape& s, int num_blocks, int max_seqs) {
+  CacheLayout c;
+  const int max_blocks = (s.max_pos + kBlock - 1) / kBlock;
+  size_t off = 0;
+  c.k = off;
+  off = align256(off + pool_bytes(s, num_blocks));
+  c.v = off;
+  off = align256(off + pool_bytes(s, num_blocks));
+  c.table = off;
+  off = align256(off + (size_t)max_seqs * max_blocks * sizeof(int32_t));
+  c.total = off;
+  return c;
+}
+
+llk::CacheView cache_view(const llama_kv_cache* c) {
+  llk::CacheView v;
+  v.k_pool = c->k_pool;
+  v.v_pool = c->v_pool;
+  v.block_table = c->table;
+  v.max_blocks = c->max_blocks;
+  v.G = c->s.G;
+  v.D = c->s.D;
+  return v;
+}
+
+// Flush (index, value) pairs to device int32 memory through kernel arguments.
+struct Uploader {
+  std::vector<llk::Upload> batches;
+  void add(int32_t* base, int32_t idx, int32_t val) {
+    if (batches.empty() || batches.back().base != base || batches.back().n == llk::kUploadMax) {
+      batches.emplace_back();
+      std::memset(&batches.back(), 0, sizeof(llk::Upload));
+      batches.back().base = base;
+    }
+    llk::Upload& u = batches.back();
+    u.idx[u.n] = idx;
+    u.val[u.n] = val;
+    ++u.n;
+  }
+  hipError_t flush(hipStream_t s) {
+    for (auto& u : batches) {
+      hipError_t e = llk::launch_upload(u, s);
+      if (e != hipSuccess) return e;
+    }
+    batches.clear();
+    return hipSuccess;
+  }
+};
+
+bool same_shape(const Shape& a, const Shape& b) {
+  return a.G == b.G && a.D == b.D && a.dt == b.dt && a.max_pos == b.max_pos;
+}
+
+// Validate a batch of sequences about to grow by n tokens each; on success
+// append the block-table updates to `up` and commit the allocation.
+llama_status reserve(llama_kv_cache* c, int batch, const int32_t* seq_ids, int n, Uploader* up) {
+  std::unordered_set<int32_t> seen;
+  long need = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int32_t id = seq_ids[b];
+    if (id < 0 || id >= c->max_seqs || !c->seqs[id].open) return LLAMA_ERR_BAD_SEQ;
+    if (!seen.insert(id).second) return LLAMA_ERR_BAD_SEQ;
+    const long new_len = (long)c->seqs[id].len + n;
+    if (new_len > c->s.max_pos) return LLAMA_ERR_POSITION;
+    need += (new_len + kBlock - 1) / kBlock - (long)c->seqs[id].blocks.size();
+  }
+  if (need > (long)c->free_blocks.size()) return LLAMA_ERR_CACHE_FULL;
+  for (int b = 0; b < batch; ++b) {
+    SeqState& st = c->seqs[seq_ids[b]];
+    const int want = (st.len + n + kBlock - 1) / kBlock;
+    while ((int)st.blocks.size() < want) {
+      const int32_t blk = c->free_blocks.back();
+      c->free_blocks.pop_back();
+      up->add(c->table, seq_ids[b] * c->max_blocks + (int32_t)st.blocks.size(), blk);
+      st.blocks.push_back(blk);
+    }
+  }
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* llama_status_string(llama_status s) {
+  switch (s) {
+    case LLAMA_OK: return "ok";
+    case LLAMA_ERR_INVALID_ARG: return "invalid argument";
+    case LLAMA_ERR_SHAPE: return "invalid shape";
+    case LLAMA_ERR_DTYPE: return "invalid dtype";
+    case LLAMA_ERR_CACHE_FULL: return "KV cache full";
+    case LLAMA_ERR_BAD_SEQ: return "bad sequence id";
+    case LLAMA_ERR_POSITION: return "position beyond max_position";
+    case LLAMA_ERR_HIP: return "HIP error";
+    case LLAMA_ERR_UNSUPPORTED: return "unsupported configuration";
+  }
+  return "unknown status";
+}
+
+llama_status llama_layer_packed_bytes(const llama_layer_config* cfg, size_t* bytes) {
+  if (!bytes) return LLAMA_ERR_INVALID_ARG;
+  Shape s;
+  llama_status st = check_config(cfg, &s);
+  if (st != LLAMA_OK) return st;
+  *bytes = packed_layout(s).total;
+  return LLAMA_OK;
+}
+
+llama_status llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights* w, void* packed_dev,
+                                void* stream, llama_layer** out) {
+  if (!out || !w || !packed_dev) return LLAMA_ERR_INVALID_ARG;
+  Shape s;
+  llama_status st = check_config(cfg, &s);
+  if (st != LLAMA_OK) return st;
+  const void* ptrs[] = {w->q_proj, w->k_proj, w->v_proj, w->o_proj, w->gate_proj,
+                        w->up_proj, w->down_proj, w->input_layernorm, w->post_attention_layernorm};
+  for (const void* p : ptrs)
+    if (!p || !aligned(p, 16)) return LLAMA_ERR_INVALID_ARG;
+  if (!aligned(packed_dev, 256)) return LLAMA_ERR_INVALID_ARG;
+
+  llama_layer* L = new (std::nothrow) llama_layer;
+  if (!L) return LLAMA_ERR_INVALID_ARG;
+  L->cfg = *cfg;
+  L->s = s;
+  L->pl = packed_layout(s);
+  L->packed = reinterpret_cast<char*>(packed_dev);
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  auto fail = [&](hipError_t e) {
+    if (trace_on()) std::fprintf(stderr, "[llama_layer] create: %s\n", hipGetErrorString(e));
+    delete L;
+    return LLAMA_ERR_HIP;
+  };
+  char* P = L->packed;
+  hipError_t e = llk::launch_zero(P, L->pl.cos, hs);  // padding rows and columns stay zero
+  // fused QKV weight with gamma_1 folded in: rows [q | k | v]
+  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->q_proj, w->input_layernorm, P + L->pl.qkv, s.HD, s.d, s.d, 1, 0, hs);
+  if (e == hipSuccess)
+    e = llk::launch_pack(s.dt, w->k_proj, w->input_layernorm, P + L->pl.qkv, s.KD, s.d, s.d, 1, s.HD, hs);
+  if (e == hipSuccess)
+    e = llk::launch_pack(s.dt, w->v_proj, w->input_layernorm, P + L->pl.qkv, s.KD, s.d, s.d, 1, s.HD + s.KD, hs);
+  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->o_proj, nullptr, P + L->pl.o, s.d, s.HD, s.HD, 1, 0, hs);
+  // gate/up interleaved row by row, gamma_2 folded in
+  if (e == hipSuccess)
+    e = llk::launch_pack(s.dt, w->gate_proj, w->post_attention_layernorm, P + L->pl.gu, s.I, s.d, s.d, 2, 0, hs);
+  if (e == hipSuccess)
+    e = llk::launch_pack(s.dt, w->up_proj, w->post_attention_layernorm, P + L->pl.gu, s.I, s.d, s.d, 2, 1, hs);
+  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->down_proj, nullptr, P + L->pl.down, s.d, s.I, s.I_pad, 1, 0, hs);
+  if (e != hipSuccess) return fail(e);
+
+  // RoPE table, angle pos * theta^(-2i/D) evaluated in double, stored fp32
+  // ("Chapter 10", section 3; "From Transformer to LLaMA: an overview", 4.2)
+  const int half = s.D / 2;
+  std::vector<float> cs((size_t)s.max_pos * half), sn((size_t)s.max_pos * half);
+  for (int i = 0; i < half; ++i) {
+    const double inv = std::pow((double)cfg->rope_theta, -2.0 * i / s.D);
+    for (int p = 0; p < s.max_pos; ++p) {
+      const double a = (double)p * inv;
+      cs[(size_t)p * half + i] = (float)std::cos(a);
+      sn[(size_t)p * half + i] = (float)std::sin(a);
+    }
+  }
+  e = llk::copy_to_device(P + L->pl.cos, cs.data(), cs.size() * sizeof(float), hs);
+  if (e == hipSuccess) e = llk::copy_to_device(P + L->pl.sin, sn.data(), sn.size() * sizeof(float), hs);
+  if (e == hipSuccess) e = llk::stream_sync(hs);
+  if (e != hipSuccess) return fail(e);
+  *out = L;
+  return LLAMA_OK;
+}
+
+llama_status llama_layer_workspace_bytes(const llama_layer* layer, int32_t max_tokens, int32_t max_batch,
+                                         size_t* bytes) {
+  if (!layer || !bytes || max_tokens <= 0 || max_batch <= 0 || max_batch > max_tokens) return LLAMA_ERR_INVALID_ARG;
+  *bytes = ws_layout(layer->s, (size_t)max_tokens, (size_t)max_batch).total;
+  return LLAMA_OK;
+}
+
+llama_status llama_layer_destroy(llama_layer* layer) {
+  if (!layer) return LLAMA_ERR_INVALID_ARG;
+  drop_events(layer);
+  delete layer;
+  return LLAMA_OK;
+}
+
+llama_status llama_layer_profile_enable(llama_layer* layer, int32_t enable) {
+  if (!layer) return LLAMA_ERR_INVALID_ARG;
+  layer->profiling = enable != 0;
+  if (!layer->profiling) {
+    drop_events(layer);
+    for (int k = 0; k < K_COUNT; ++k) {
+      layer->launches[k] = 0;
+      layer->total_ms[k] = 0.0;
+    }
+  }
+  return LLAMA_OK;
+}
+
+llama_status llama_layer_profile_read(llama_layer* layer, llama_kernel_time* out, int32_t max, int32_t* n,
+                                      int32_t reset) {
+  if (!layer || !n || max < 0 || (max > 0 && !out)) return LLAMA_ERR_INVALID_ARG;
+  for (auto& p : layer->pending) {
+    float ms = 0.f;
+    HIP_TRY(llk::event_elapsed_ms(&ms, p.start, p.stop));
+    layer->launches[p.kind] += 1;
+    layer->total_ms[p.kind] += ms;
+    layer->free_events.push_back(p.start);
+    layer->free_events.push_back(p.stop);
+  }
+  layer->pending.clear();
+  int cnt = 0;
+  for (int k = 0; k < K_COUNT; ++k) {
+    if (layer->launches[k] == 0) continue;
+    if (cnt < max) {
+      std::memset(&out[cnt], 0, sizeof(llama_kernel_time));
+      std::snprintf(out[cnt].name, sizeof(out[cnt].name), "%s", kKernNames[k]);
+      out[cnt].launches = layer->launches[k];
+      out[cnt].total_ms = layer->total_ms[k];
+    }
+    ++cnt;
+  }
+  *n = cnt < max ? cnt : max;
+  if (reset) {
+    for (int k = 0; k < K_COUNT; ++k) {
+      layer->launches[k] = 0;
+      layer->total_ms[k] = 0.0;
+    }
+  }
+  return LLAMA_OK;
+}
+
+// ---- cache ----------------------------------------------------------------
+
+llama_status llama_kv_cache_bytes(const llama_layer_config* cfg, int32_t num_blocks, int32_t block_size,
+                                  int32_t max_seqs, size_t* bytes) {
+  if (!bytes || num_blocks <= 0 || max_seqs <= 0) return LLAMA_ERR_INVALID_ARG;
+  Shape s;
+  llama_status st = check_config(cfg, &s);
+  if (st != LLAMA_OK) return st;
+  if (block_size != kBlock) return LLAMA_ERR_UNSUPPORTED;
+  *bytes = cache_layout(s, num_blocks, max_seqs).total;
+  return LLAMA_OK;
+}
+
+llama_status llama_kv_cache_create(const llama_layer_config* cfg, int32_t num_blocks, int32_t block_size,
+                                   int32_t max_seqs, const int32_t* block_order, void* pool_dev,
+                                   llama_kv_cache** out) {
+  if (!out || !pool_dev || num_blocks <= 0 || max_seqs <= 0) return LLAMA_ERR_INVALID_ARG;
+  if (!aligned(pool_dev, 256)) return LLAMA_ERR_INVALID_ARG;
+  Shape s;
+  llama_status st = check_config(cfg, &s);
+  if (st != LLAMA_OK) return st;
+  if (block_size != kBlock) return LLAMA_ERR_UNSUPPORTED;
+  std::vector<int32_t> order(num_blocks);
+  if (block_order) {
+    std::vector<char> hit(num_blocks, 0);
+    for (int i = 0; i < num_blocks; ++i) {
+      const int32_t b = block_order[i];
+      if (b < 0 || b >= num_blocks || hit[b]) return LLAMA_ERR_INVALID_ARG;
+      hit[b] = 1;
+      order[i] = b;
+    }
+  } else {
+    for (int i = 0; i < num_blocks; ++i) order[i] = i;
+  }
+  llama_kv_cache* c = new (std::nothrow) llama_kv_cache;
+  if (!c) return LLAMA_ERR_INVALID_ARG;
+  const CacheLayout cl = cache_layout(s, num_blocks, max_seqs);
+  c->s = s;
+  c->num_blocks = num_blocks;
+  c->max_seqs = max_seqs;
+  c->max_blocks = (s.max_pos + kBlock - 1) / kBlock;
+  c->k_pool = reinterpret_cast<char*>(pool_dev) + cl.k;
+  c->v_pool = reinterpret_cast<char*>(pool_dev) + cl.v;
+  c->table = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(pool_dev) + cl.table);
+  c->free_blocks.assign(order.rbegin(), order.rend());
+  c->seqs.resize(max_seqs);
+  *out = c;
+  return LLAMA_OK;
+}
+
+llama_status llama_kv_cache_destroy(llama_kv_cache* cache) {
+  if (!cache) return LLAMA_ERR_INVALID_ARG;
+  delete cache;
+  return LLAMA_OK;
+}
+
+llama_status llama_kv_cache_add_seq(llama_kv_cache* c, int32_t* seq_id_out) {
+  if (!c || !seq_id_out) return LLAMA_ERR_INVALID_ARG;
+  for (int i = 0; i < c->max_seqs; ++i) {
+    if (!c->seqs[i].open) {
+      c->seqs[i].open = true;
+      c->seqs[i].len = 0;
+      c->seqs[i].blocks.clear();
+      *seq_id_out = i;
+      return LLAMA_OK;
+    }
+  }
+  return LLAMA_ERR_CACHE_FULL;
+}
+
+llama_status llama_kv_cache_free_seq(llama_kv_cache* c, int32_t seq_id) {
+  if (!c) return LLAMA_ERR_INVALID_ARG;
+  if (seq_id < 0 || seq_id >= c->max_seqs || !c->seqs[seq_id].open) return LLAMA_ERR_BAD_SEQ;
+  SeqState& st = c->seqs[seq_id];
+  for (auto it = st.blocks.rbegin(); it != st.blocks.rend(); ++it) c->free_blocks.push_back(*it);
+  st = SeqState();
+  return LLAMA_OK;
+}
+
+llama_status llama_kv_cache_seq_len(const llama_kv_cache* c, int32_t seq_id, int32_t* len) {
+  if (!c || !len) return LLAMA_ERR_INVALID_ARG;
+  if (seq_id < 0 || seq_id >= c->max_seqs || !c->seqs[seq_id].open) return LLAMA_ERR_BAD_SEQ;
+  *len = c->seqs[seq_id].len;
+  return LLAMA_OK;
+}
+
+llama_status llama_kv_cache_free_blocks(const llama_kv_cache* c, int32_t* n) {
+  if (!c || !n) return LLAMA_ERR_INVALID_ARG;
+  *n = (int32_t)c->free_blocks.size();
+  return LLAMA_OK;
+}
+
+llama_status llama_kv_cache_write(llama_kv_cache* c, int32_t seq_id, int32_t n_tokens, const void* k_dev,
+                                  const void* v_dev, void* stream) {
+  if (!c || !k_dev || !v_dev || n_tokens <= 0) return LLAMA_ERR_INVALID_ARG;
+  Uploader up;
+  const int start = (seq_id >= 0 && seq_id < c->max_seqs) ? c->seqs[seq_id].len : 0;
+  llama_status st = reserve(c, 1, &seq_id, n_tokens, &up);
+  if (st != LLAMA_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  HIP_TRY(up.flush(hs));
+  HIP_TRY(llk::launch_kv_copy(c->s.dt, cache_view(c), seq_id, start, n_tokens, const_cast<void*>(k_dev),
+                              const_cast<void*>(v_dev), true, hs));
+  c->seqs[seq_id].len += n_tokens;
+  return LLAMA_OK;
+}
+
+llama_status llama_kv_cache_read(const llama_kv_cache* c, int32_t seq_id, int32_t start, int32_t n, void* k_dev,
+                                 void* v_dev, void* stream) {
+  if (!c || !k_dev || !v_dev || n <= 0 || start < 0) return LLAMA_ERR_INVALID_ARG;
+  if (seq_id < 0 || seq_id >= c->max_seqs || !c->seqs[seq_id].open) return LLAMA_ERR_BAD_SEQ;
+  if ((long)start + n > c->seqs[seq_id].len) return LLAMA_ERR_POSITION;
+  HIP_TRY(llk::launch_kv_copy(c->s.dt, cache_view(c), seq_id, start, n, k_dev, v_dev, false,
+                              reinterpret_cast<hipStream_t>(stream)));
+  return LLAMA_OK;
+}
+
+// ---- forward ----------------------------------------------------------------
+
+static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, int32_t seq_len,
+                            const int32_t* seq_ids, const void* x, void* out, int32_t out_dtype, void* workspace,
+                            void* stream, bool decode) {
+  if (!L || !c || !seq_ids || !x || !out || !workspace) return LLAMA_ERR_INVALID_ARG;
+  if (batch <= 0 || seq_len <= 0) return LLAMA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, 256)) return LLAMA_ERR_INVALID_ARG;
+  if (out_dtype != LLAMA_DTYPE_F32 && out_dtype != LLAMA_DTYPE_BF16) return LLAMA_ERR_DTYPE;
+  if (L->s.dt == DType::F32 && out_dtype != LLAMA_DTYPE_F32) return LLAMA_ERR_DTYPE;
+  if (!same_shape(L->s, c->s)) return LLAMA_ERR_SHAPE;
+  const long T = (long)batch * seq_len;
+  if (T > (1L << 24)) return LLAMA_ERR_SHAPE;
+  const Shape& s = L->s;
+
+  std::vector<int32_t> start(batch);
+  for (int b = 0; b < batch; ++b)
+    start[b] = (seq_ids[b] >= 0 && seq_ids[b] < c->max_seqs) ? c->seqs[seq_ids[b]].len : 0;
+  Uploader up;
+  llama_status st = reserve(c, batch, seq_ids, seq_len, &up);
+  if (st != LLAMA_OK) return st;
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const WsLayout wl = ws_layout(s, (size_t)T, (size_t)batch);
+  char* W = reinterpret_cast<char*>(workspace);
+  int32_t* desc = reinterpret_cast<int32_t*>(W + wl.desc);
+  for (int b = 0; b < batch; ++b) {
+    up.add(desc, 2 * b, seq_ids[b]);
+    up.add(desc, 2 * b + 1, start[b]);
+  }
+  // lengths are committed now: every later failure is a device failure
+  for (int b = 0; b < batch; ++b) c->seqs[seq_ids[b]].len += seq_len;
+  HIP_TRY(up.flush(hs));
+
+  float* r1 = reinterpret_cast<float*>(W + wl.r1);
+  float* r2 = reinterpret_cast<float*>(W + wl.r2);
+  void* qb = W + wl.q;
+  void* attn = W + wl.attn;
+  float* h = reinterpret_cast<float*>(W + wl.h);
+  void* hb = W + wl.hb;
+  void* sb = W + wl.s;
+  float* part = reinterpret_cast<float*>(W + wl.part);
+  const char* P = L->packed;
+  const float eps = L->cfg.rms_norm_eps;
+  const int M = (int)T;
+
+  llk::BatchView bv{desc, batch, seq_len};
+  llk::CacheView cv = cache_view(c);
+  auto tile_for = [&](int N) {
+    return (M >= 256 && N % llk::gemm_tile_n(llk::GemmTile::LARGE) == 0) ? llk::GemmTile::LARGE
+                                                                          : llk::GemmTile::SMALL;
+  };
+  if (trace_on())
+    std::fprintf(stderr, "[llama_layer] %s B=%d S=%d T=%d d=%d H=%d G=%d D=%d I=%d\n", decode ? "decode" : "prefill",
+                 batch, seq_len, M, s.d, s.H, s.G, s.D, s.I);
+
+  // RMSNorm_1 statistics
+  HIP_TRY(timed(L, K_RMS1, hs, [&] { return llk::launch_rms_rowscale(s.dt, x, r1, M, s.d, eps, hs); }));
+
+  // QKV + RoPE + cache append
+  llk::GemmArgs a{};
+  a.W = P + L->pl.qkv;
+  a.X = x;
+  a.M = M;
+  a.N = s.NQKV_pad;
+  a.K = s.d;
+  a.ldx = s.d;
+  a.epi = llk::Epi::QKV;
+  a.rowscale = r1;
+  a.q_out = qb;
+  a.cache = cv;
+  a.batch = bv;
+  a.rope_cos = reinterpret_cast<const float*>(P + L->pl.cos);
+  a.rope_sin = reinterpret_cast<const float*>(P + L->pl.sin);
+  a.H = s.H;
+  HIP_TRY(timed(L, K_QKV, hs, [&] { return llk::launch_gemm(s.dt, tile_for(a.N), a, hs); }));
+
+  // attention
+  if (decode) {
+    const int ms = max_splits_for(s);
+    HIP_TRY(timed(L, K_ATTN_DECODE, hs, [&] { return llk::launch_attn_decode(s.dt, qb, part, ms, s.H, cv, bv, hs); }));
+    HIP_TRY(timed(L, K_ATTN_COMBINE, hs,
+                  [&] { return llk::launch_attn_decode_combine(s.dt, part, attn, ms, s.H, s.D, bv, hs); }));
+  } else {
+    HIP_TRY(timed(L, K_ATTN_PREFILL, hs, [&] { return llk::launch_attn_prefill(s.dt, qb, attn, s.H, cv, bv, hs); }));
+  }
+
+  // o_proj + residual -> h (fp32)
+  llk::GemmArgs o{};
+  o.W = P + L->pl.o;
+  o.X = attn;
+  o.M = M;
+  o.N = s.d;
+  o.K = s.HD;
+  o.ldx = s.HD;
+  o.epi = llk::Epi::RESID_H;
+  o.resid = x;
+  o.out = h;
+  o.ldo = s.d;
+  HIP_TRY(timed(L, K_OPROJ, hs, [&] { return llk::launch_gemm(s.dt, tile_for(o.N), o, hs); }));
+
+  // RMSNorm_2 statistics + operand copy
+  HIP_TRY(timed(L, K_RMS2, hs, [&] { return llk::launch_rms_convert(s.dt, h, hb, r2, M, s.d, eps, hs); }));
+
+  // gate/up + SiLU * up
+  llk::GemmArgs g{};
+  g.W = P + L->pl.gu;
+  g.X = hb;
+  g.M = M;
+  g.N = 2 * s.I_pad;
+  g.K = s.d;
+  g.ldx = s.d;
+  g.epi = llk::Epi::SWIGLU;
+  g.rowscale = r2;
+  g.out = sb;
+  g.ldo = s.I_pad;
+  HIP_TRY(timed(L, K_GATEUP, hs, [&] { return llk::launch_gemm(s.dt, tile_for(g.N), g, hs); }));
+
+  // down + residual -> out
+  llk::GemmArgs dn{};
+  dn.W = P + L->pl.down;
+  dn.X = sb;
+  dn.M = M;
+  dn.N = s.d;
+  dn.K = s.I_pad;
+  dn.ldx = s.I_pad;
+  dn.epi = llk::Epi::RESID_OUT;
+  dn.resid = h;
+  dn.out = out;
+  dn.ldo = s.d;
+  dn.out_dtype = out_dtype == LLAMA_DTYPE_F32 ? DType::F32 : DType::BF16;
+  HIP_TRY(timed(L, K_DOWN, hs, [&] { return llk::launch_gemm(s.dt, tile_for(dn.N), dn, hs); }));
+  return LLAMA_OK;
+}
+
+llama_status llama_layer_prefill(llama_layer* layer, llama_kv_cache* cache, int32_t batch, int32_t seq_len,
+                                 const int32_t* seq_ids, const void* x, void* out, int32_t out_dtype,
+                                 void* workspace, void* stream) {
+  return forward(layer, cache, batch, seq_len, seq_ids, x, out, out_dtype, workspace, stream, false);
+}
+
+llama_status llama_layer_decode(llama_layer* layer, llama_kv_cache* cache, int32_t batch, const int32_t* seq_ids,
+                                const void* x, void* out, int32_t out_dtype, void* workspace, void* stream) {
+  return forward(layer, cache, batch, 1, seq_ids, x, out, out_dtype, workspace, stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// RMSNorm row statistics for the decoder layer.
+//
+// RMSNorm(x) = x * rsqrt(mean(x^2) + eps) * gamma with the statistics in fp32
+// ("Chapter 10: the modern LLaMA architecture", section 4; "3.2 Core
+// components, one by one", 3.2.1).  gamma is folded into the weights of the
+// projection that follows, and the row scale r is applied in that GEMM's
+// epilogue, so the norm itself is one HBM pass that writes 4 bytes per row.
+// One wavefront per row, 16-byte loads, shuffle reduction.
+#include "common.h"
+#include "kernels.h"
+
+namespace llk {
+namespace {
+
+DEVI float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += shfl_xor(v, m);
+  return v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void rms_rowscale_kernel(const T* __restrict__ x, float* __restrict__ r,
+                                                           int M, int d, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const T* p = x + (size_t)row * d;
+  float acc = 0.f;
+  for (int c = lane * Chunk<T>::N; c < d; c += 64 * Chunk<T>::N) {
+    auto v = load_chunk<T>(p + c);
+#pragma unroll
+    for (int e = 0; e < Chunk<T>::N; ++e) {
+      const float f = to_f32(v[e]);
+      acc += f * f;
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) r[row] = 1.f / sqrtf(acc / (float)d + eps);
+}
+
+// Second norm: statistics of the fp32 residual stream h, plus h stored in the
+// layer dtype as the next GEMM's operand.
+template <typename T>
+__global__ __launch_bounds__(256) void rms_convert_kernel(const float* __restrict__ h, T* __restrict__ hb,
+                                                          float* __restrict__ r, int M, int d, float eps) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const float* p = h + (size_t)row * d;
+  T* q = hb + (size_t)row * d;
+  float acc = 0.f;
+  for (int c = lane * 4; c < d; c += 64 * 4) {
+    f32x4 v = *reinterpret_cast<const f32x4*>(p + c);
+    acc += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    if constexpr (sizeof(T) == 4) {
+      *reinterpret_cast<f32x4*>(q + c) = v;
+    } else {
+      *reinterpret_cast<bf16x4*>(q + c) =
+          bf16x4{from_f32<bf16>(v[0]), from_f32<bf16>(v[1]), from_f32<bf16>(v[2]), from_f32<bf16>(v[3])};
+    }
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) r[row] = 1.f / sqrtf(acc / (float)d + eps);
+}
+
+}  // namespace
+
+hipError_t launch_rms_rowscale(DType t, const void* x, float* r, int M, int d, float eps, hipStream_t s) {
+  const int grid = (M + 3) / 4;
+  if (t == DType::BF16)
+    rms_rowscale_kernel<bf16><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(x), r, M, d, eps);
+  else
+    rms_rowscale_kernel<float><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(x), r, M, d, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_rms_convert(DType t, const float* h, void* hb, float* r, int M, int d, float eps,
+                              hipStream_t s) {
+  const int grid = (M + 3) / 4;
+  if (t == DType::BF16)
+    rms_convert_kernel<bf16><<<grid, 256, 0, s>>>(h, reinterpret_cast<bf16*>(hb), r, M, d, eps);
+  else
+    rms_convert_kernel<float><<<grid, 256, 0, s>>>(h, reinterpret_cast<float*>(hb), r, M, d, eps);
+  return hipGetLastError();
+}
+
+}  // namespace llk

@@ -1,0 +1,324 @@
+// Host-only check of the library's runtime (validation, block manager, packing
+// plan, RoPE table, uploads, paged K/V copies) under ASan/UBSan.  The kernel
+// launch interface is replaced by stubs that run on host memory: "device"
+// buffers are plain host allocations, uploads and K/V copies are executed, and
+// compute launches are only recorded.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "llama_layer.h"
+#include "../../decoder_block_amd/csrc/kernels.h"
+
+static int g_fail = 0;
+#define CHECK(c)                                                        \
+  do {                                                                  \
+    if (!(c)) {                                                         \
+      std::fprintf(stderr, "CHECK failed %s:%d: %s\n", __FILE__, __LINE__, #c); \
+      ++g_fail;                                                         \
+    }                                                                   \
+  } while (0)
+
+static std::vector<std::string> g_log;
+static int g_events = 0;
+struct PackCall { int rows, cols, ldd, row_mul, row_add; bool gamma; };
+static std::vector<PackCall> g_packs;
+
+namespace llk {
+int gemm_tile_n(GemmTile t) { return t == GemmTile::LARGE ? 256 : 64; }
+hipError_t launch_gemm(DType, GemmTile t, const GemmArgs& a, hipStream_t) {
+  g_log.push_back("gemm" + std::to_string((int)a.epi) + (t == GemmTile::LARGE ? "L" : "S"));
+  return hipSuccess;
+}
+hipError_t launch_rms_rowscale(DType, const void*, float*, int, int, float, hipStream_t) {
+  g_log.push_back("rms1");
+  return hipSuccess;
+}
+hipError_t launch_rms_convert(DType, const float*, void*, float*, int, int, float, hipStream_t) {
+  g_log.push_back("rms2");
+  return hipSuccess;
+}
+hipError_t launch_attn_prefill(DType, const void*, void*, int, const CacheView&, const BatchView&, hipStream_t) {
+  g_log.push_back("attn_prefill");
+  return hipSuccess;
+}
+int decode_split_keys() { return 1024; }
+hipError_t launch_attn_decode(DType, const void*, float*, int, int, const CacheView&, const BatchView&, hipStream_t) {
+  g_log.push_back("attn_decode");
+  return hipSuccess;
+}
+hipError_t launch_attn_decode_combine(DType, const float*, void*, int, int, int, const BatchView&, hipStream_t) {
+  g_log.push_back("attn_combine");
+  return hipSuccess;
+}
+hipError_t event_create(void** ev) {
+  *ev = std::malloc(8);
+  ++g_events;
+  return hipSuccess;
+}
+hipError_t event_destroy(void* ev) {
+  std::free(ev);
+  --g_events;
+  return hipSuccess;
+}
+hipError_t event_record(void*, hipStream_t) { return hipSuccess; }
+hipError_t event_elapsed_ms(float* ms, void*, void*) {
+  *ms = 0.5f;
+  return hipSuccess;
+}
+hipError_t launch_pack(DType, const void*, const void* gamma, void*, int rows, int cols, int ldd, int row_mul,
+                       int row_add, hipStream_t) {
+  g_packs.push_back({rows, cols, ldd, row_mul, row_add, gamma != nullptr});
+  return hipSuccess;
+}
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t) {
+  std::memset(dst, 0, bytes);
+  return hipSuccess;
+}
+hipError_t launch_upload(const Upload& u, hipStream_t) {
+  for (int i = 0; i < u.n; ++i) u.base[u.idx[i]] = u.val[i];
+  return hipSuccess;
+}
+hipError_t copy_to_device(void* dst, const void* src, size_t bytes, hipStream_t) {
+  std::memcpy(dst, src, bytes);
+  return hipSuccess;
+}
+hipError_t stream_sync(hipStream_t) { return hipSuccess; }
+hipError_t launch_kv_copy(DType t, const CacheView& c, int seq, int start, int n, void* k, void* v, bool to_cache,
+                          hipStream_t) {
+  const size_t es = t == DType::F32 ? 4 : 2;
+  char* kp = (char*)c.k_pool;
+  char* vp = (char*)c.v_pool;
+  for (int i = 0; i < n; ++i)
+    for (int g = 0; g < c.G; ++g)
+      for (int d = 0; d < c.D; ++d) {
+        const int pos = start + i;
+        const size_t blk = (size_t)c.block_table[(size_t)seq * c.max_blocks + pos / 16];
+        const size_t ko = ((blk * c.G + g) * 16 + pos % 16) * c.D + d;
+        const size_t vo = ((blk * c.G + g) * c.D + d) * 16 + pos % 16;
+        const size_t lo = ((size_t)i * c.G + g) * c.D + d;
+        if (to_cache) {
+          std::memcpy(kp + ko * es, (char*)k + lo * es, es);
+          std::memcpy(vp + vo * es, (char*)v + lo * es, es);
+        } else {
+          std::memcpy((char*)k + lo * es, kp + ko * es, es);
+          std::memcpy((char*)v + lo * es, vp + vo * es, es);
+        }
+      }
+  return hipSuccess;
+}
+}  // namespace llk
+
+static void* aligned_buf(size_t n) {
+  void* p = nullptr;
+  if (posix_memalign(&p, 256, n ? n : 256) != 0) std::abort();
+  std::memset(p, 0, n);
+  return p;
+}
+
+static llama_layer_config tiny(llama_dtype dt = LLAMA_DTYPE_F32) {
+  llama_layer_config c;
+  c.hidden_size = 256;
+  c.intermediate_size = 688;
+  c.num_attention_heads = 4;
+  c.num_key_value_heads = 2;
+  c.rms_norm_eps = 1e-5f;
+  c.rope_theta = 10000.f;
+  c.max_position = 80;
+  c.dtype = dt;
+  return c;
+}
+
+int main() {
+  size_t bytes = 0;
+  // ---- config validation ----
+  llama_layer_config c = tiny();
+  CHECK(llama_layer_packed_bytes(&c, &bytes) == LLAMA_OK && bytes > 0);
+  c.num_key_value_heads = 3;
+  CHECK(llama_layer_packed_bytes(&c, &bytes) == LLAMA_ERR_SHAPE);  // H % G != 0
+  c = tiny();
+  c.hidden_size = 260;
+  CHECK(llama_layer_packed_bytes(&c, &bytes) == LLAMA_ERR_SHAPE);  // d % H != 0
+  c = tiny();
+  c.dtype = 7;
+  CHECK(llama_layer_packed_bytes(&c, &bytes) == LLAMA_ERR_DTYPE);
+  c = tiny();
+  c.rms_norm_eps = 0.f;
+  CHECK(llama_layer_packed_bytes(&c, &bytes) == LLAMA_ERR_INVALID_ARG);
+  c = tiny();
+  c.hidden_size = 4 * 96;  // D = 96
+  CHECK(llama_layer_packed_bytes(&c, &bytes) == LLAMA_ERR_UNSUPPORTED);
+  c = tiny();
+  CHECK(llama_layer_packed_bytes(nullptr, &bytes) == LLAMA_ERR_INVALID_ARG);
+  CHECK(llama_kv_cache_bytes(&c, 8, 32, 2, &bytes) == LLAMA_ERR_UNSUPPORTED);
+
+  // ---- create: packing plan and RoPE table ----
+  c = tiny();
+  CHECK(llama_layer_packed_bytes(&c, &bytes) == LLAMA_OK);
+  void* packed = aligned_buf(bytes);
+  std::vector<void*> wbufs;
+  llama_layer_weights w;
+  const void** wp = reinterpret_cast<const void**>(&w);
+  for (int i = 0; i < 9; ++i) {
+    wbufs.push_back(aligned_buf(256 * 1024 * 4));
+    wp[i] = wbufs.back();
+  }
+  llama_layer* L = nullptr;
+  llama_layer_weights wnull = w;
+  wnull.up_proj = nullptr;
+  CHECK(llama_layer_create(&c, &wnull, packed, nullptr, &L) == LLAMA_ERR_INVALID_ARG && L == nullptr);
+  CHECK(llama_layer_create(&c, &w, packed, nullptr, &L) == LLAMA_OK && L != nullptr);
+  CHECK(g_packs.size() == 7);
+  if (g_packs.size() == 7) {
+    // q, k, v rows stacked; gate/up interleaved; down padded to a multiple of 128 columns
+    CHECK(g_packs[0].rows == 256 && g_packs[0].row_add == 0 && g_packs[0].gamma);
+    CHECK(g_packs[1].rows == 128 && g_packs[1].row_add == 256 && g_packs[1].gamma);
+    CHECK(g_packs[2].rows == 128 && g_packs[2].row_add == 384 && g_packs[2].gamma);
+    CHECK(!g_packs[3].gamma && g_packs[3].rows == 256);
+    CHECK(g_packs[4].row_mul == 2 && g_packs[4].row_add == 0 && g_packs[4].gamma);
+    CHECK(g_packs[5].row_mul == 2 && g_packs[5].row_add == 1 && g_packs[5].gamma);
+    CHECK(g_packs[6].cols == 688 && g_packs[6].ldd == 768 && !g_packs[6].gamma);
+  }
+  // the RoPE tables are the last two sections of the packed buffer
+  {
+    const int half = 32, P = 80;
+    const size_t tbl = (size_t)P * half * sizeof(float);
+    const size_t sin_off = bytes - ((tbl + 255) & ~size_t(255));
+    const size_t cos_off = sin_off - ((tbl + 255) & ~size_t(255));
+    const float* cs = (const float*)((char*)packed + cos_off);
+    const float* sn = (const float*)((char*)packed + sin_off);
+    for (int p : {0, 1, 37, 79})
+      for (int i : {0, 1, 17, 31}) {
+        const double a = p * std::pow(10000.0, -2.0 * i / 64);
+        CHECK(std::fabs(cs[p * half + i] - (float)std::cos(a)) < 1e-7);
+        CHECK(std::fabs(sn[p * half + i] - (float)std::sin(a)) < 1e-7);
+      }
+  }
+  size_t wsb = 0;
+  CHECK(llama_layer_workspace_bytes(L, 64, 1, &wsb) == LLAMA_OK && wsb > 0);
+  CHECK(llama_layer_workspace_bytes(L, 4, 8, &wsb) == LLAMA_ERR_INVALID_ARG);
+
+  // ---- cache ----
+  const int NB = 9;
+  CHECK(llama_kv_cache_bytes(&c, NB, 16, 3, &bytes) == LLAMA_OK);
+  void* pool = aligned_buf(bytes);
+  llama_kv_cache* C = nullptr;
+  int32_t bad_order[NB];
+  for (int i = 0; i < NB; ++i) bad_order[i] = i % 6;
+  CHECK(llama_kv_cache_create(&c, NB, 16, 3, bad_order, pool, &C) == LLAMA_ERR_INVALID_ARG);
+  int32_t order[NB] = {5, 8, 2, 7, 0, 3, 1, 6, 4};
+  CHECK(llama_kv_cache_create(&c, NB, 16, 3, order, pool, &C) == LLAMA_OK);
+  int32_t s0 = -1, s1 = -1, s2 = -1, s3 = -1, n = 0;
+  CHECK(llama_kv_cache_add_seq(C, &s0) == LLAMA_OK && s0 == 0);
+  CHECK(llama_kv_cache_add_seq(C, &s1) == LLAMA_OK && s1 == 1);
+  CHECK(llama_kv_cache_add_seq(C, &s2) == LLAMA_OK && s2 == 2);
+  CHECK(llama_kv_cache_add_seq(C, &s3) == LLAMA_ERR_CACHE_FULL);
+  CHECK(llama_kv_cache_free_seq(C, s2) == LLAMA_OK);
+  CHECK(llama_kv_cache_free_seq(C, s2) == LLAMA_ERR_BAD_SEQ);
+
+  // prefill 2 x 20 tokens: 2 blocks each, handed out in `order`
+  void* ws = aligned_buf(1 << 22);
+  void* x = aligned_buf(2 * 20 * 256 * 4);
+  void* out = aligned_buf(2 * 20 * 256 * 4);
+  int32_t ids[2] = {s0, s1};
+  g_log.clear();
+  CHECK(llama_layer_prefill(L, C, 2, 20, ids, x, out, LLAMA_DTYPE_BF16, ws, nullptr) == LLAMA_ERR_DTYPE);
+  CHECK(llama_layer_prefill(L, C, 2, 20, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+  {
+    const std::vector<std::string> want = {"rms1", "gemm0S", "attn_prefill", "gemm1S", "rms2", "gemm2S", "gemm3S"};
+    CHECK(g_log == want);
+  }
+  CHECK(llama_kv_cache_seq_len(C, s0, &n) == LLAMA_OK && n == 20);
+  CHECK(llama_kv_cache_free_blocks(C, &n) == LLAMA_OK && n == NB - 4);
+  // block table rows: seq 0 got order[0], order[1]; seq 1 got order[2], order[3]
+  size_t tab_off = 0;
+  {
+    size_t kvb = (size_t)NB * 2 * 16 * 64 * 4;
+    tab_off = 2 * ((kvb + 255) & ~size_t(255));
+  }
+  const int32_t* tab = (const int32_t*)((char*)pool + tab_off);
+  const int maxb = 5;  // ceil(80 / 16)
+  CHECK(tab[0 * maxb + 0] == 5 && tab[0 * maxb + 1] == 8);
+  CHECK(tab[1 * maxb + 0] == 2 && tab[1 * maxb + 1] == 7);
+  const int32_t* desc = (const int32_t*)ws;
+  CHECK(desc[0] == s0 && desc[1] == 0 && desc[2] == s1 && desc[3] == 0);
+
+  // errors leave the state unchanged
+  int32_t dup[2] = {s0, s0};
+  CHECK(llama_layer_prefill(L, C, 2, 4, dup, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_ERR_BAD_SEQ);
+  int32_t unk[1] = {2};
+  CHECK(llama_layer_decode(L, C, 1, unk, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_ERR_BAD_SEQ);
+  CHECK(llama_layer_prefill(L, C, 1, 61, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_ERR_POSITION);
+  CHECK(llama_layer_prefill(L, C, 2, 60, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_ERR_CACHE_FULL);
+  CHECK(llama_kv_cache_seq_len(C, s0, &n) == LLAMA_OK && n == 20);
+  CHECK(llama_kv_cache_free_blocks(C, &n) == LLAMA_OK && n == NB - 4);
+  CHECK(llama_layer_prefill(L, C, 1, 4, ids, (char*)x + 4, out, LLAMA_DTYPE_F32, ws, nullptr) ==
+        LLAMA_ERR_INVALID_ARG);
+
+  // decode: 12 steps on seq 0 (20 -> 32 crosses into a third block only at 32)
+  g_log.clear();
+  for (int t = 0; t < 12; ++t)
+    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+  CHECK(llama_kv_cache_seq_len(C, s0, &n) == LLAMA_OK && n == 32);
+  CHECK(llama_kv_cache_free_blocks(C, &n) == LLAMA_OK && n == NB - 4);
+  CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+  CHECK(llama_kv_cache_free_blocks(C, &n) == LLAMA_OK && n == NB - 5);
+  CHECK(tab[0 * maxb + 2] == 0);  // order[4]
+  CHECK(desc[0] == s0 && desc[1] == 32);
+  CHECK(g_log.size() == 13 * 8 && g_log[2] == "attn_decode" && g_log[3] == "attn_combine");
+
+  // per-kernel timing: two events per launch, totals per kernel family
+  {
+    CHECK(llama_layer_profile_enable(L, 1) == LLAMA_OK);
+    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+    llama_kernel_time kt[16];
+    int32_t nk = 0;
+    CHECK(llama_layer_profile_read(L, kt, 16, &nk, 1) == LLAMA_OK && nk == 8);
+    bool seen = false;
+    for (int i = 0; i < nk; ++i) {
+      CHECK(kt[i].launches == 2 && std::fabs(kt[i].total_ms - 1.0) < 1e-9);
+      if (std::string(kt[i].name) == "attn_decode_split") seen = true;
+    }
+    CHECK(seen);
+    CHECK(llama_layer_profile_read(L, kt, 16, &nk, 0) == LLAMA_OK && nk == 0);
+    CHECK(llama_layer_profile_enable(L, 0) == LLAMA_OK);
+    CHECK(g_events == 0);
+  }
+
+  // K/V write then read back through the paged layout
+  {
+    int32_t s = -1;
+    CHECK(llama_kv_cache_free_seq(C, s1) == LLAMA_OK);
+    CHECK(llama_kv_cache_add_seq(C, &s) == LLAMA_OK);
+    const int ntok = 37, G = 2, D = 64;
+    std::vector<float> k(ntok * G * D), v(ntok * G * D), k2(ntok * G * D), v2(ntok * G * D);
+    for (size_t i = 0; i < k.size(); ++i) {
+      k[i] = (float)i;
+      v[i] = -(float)i;
+    }
+    CHECK(llama_kv_cache_write(C, s, 30, k.data(), v.data(), nullptr) == LLAMA_OK);
+    CHECK(llama_kv_cache_write(C, s, 7, k.data() + 30 * G * D, v.data() + 30 * G * D, nullptr) == LLAMA_OK);
+    CHECK(llama_kv_cache_read(C, s, 0, ntok, k2.data(), v2.data(), nullptr) == LLAMA_OK);
+    CHECK(k == k2 && v == v2);
+    CHECK(llama_kv_cache_read(C, s, 30, 8, k2.data(), v2.data(), nullptr) == LLAMA_ERR_POSITION);
+  }
+  CHECK(llama_kv_cache_free_seq(C, s0) == LLAMA_OK);
+  CHECK(llama_kv_cache_destroy(C) == LLAMA_OK);
+  CHECK(llama_layer_destroy(L) == LLAMA_OK);
+  std::free(pool);
+  std::free(ws);
+  std::free(x);
+  std::free(out);
+  std::free(packed);
+  for (void* p : wbufs) std::free(p);
+  if (g_fail) {
+    std::fprintf(stderr, "%d checks failed\n", g_fail);
+    return 1;
+  }
+  std::printf("host_check: all checks passed\n");
+  return 0;
+}

@@ -1,0 +1,69 @@
+"""Shared helpers of the GPU parity tests and the smoke check: run the C-ABI
+library on seeded workloads and compare with the float64 oracle."""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import torch
+
+import oracle
+from decoder_block_amd import synth
+
+# Tolerances, errors divided by the RMS of the oracle output ("unit-scale"):
+#   fp32 layer: max |gpu - oracle| / RMS <= 1e-4
+#   bf16 layer: max <= 3e-2 and mean <= 3e-3
+TOL = {"f32": {"max_rel": 1e-4}, "bf16": {"max_rel": 3e-2, "mean_rel": 3e-3}}
+
+
+def errors(gpu, ref) -> dict:
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    d = np.abs(g - r)
+    rms = float(np.sqrt(np.mean(r * r)))
+    return {"max_abs": float(d.max()), "mean_abs": float(d.mean()), "rms": rms,
+            "max_rel": float(d.max()) / rms, "mean_rel": float(d.mean()) / rms,
+            "finite": bool(np.isfinite(g).all())}
+
+
+def assert_close(gpu, ref, dtype: str, what: str = "") -> dict:
+    e = errors(gpu, ref)
+    assert e["finite"], f"{what}: non-finite GPU output"
+    for k, lim in TOL[dtype].items():
+        assert e[k] <= lim, f"{what}: {k}={e[k]:.3e} > {lim:.1e} ({e})"
+    return e
+
+
+@functools.lru_cache(maxsize=2)
+def weights_for(w: synth.Workload, gamma_std: float | None = None):
+    """(storage tensors on CPU, float64 arrays for the oracle) of a workload's weights."""
+    ws = synth.layer_weights(w, gamma_std)
+    return ws, {k: synth.as_f64(v) for k, v in ws.items()}
+
+
+def make_layer(w: synth.Workload, ws: dict, max_position: int | None = None):
+    from decoder_block_amd.llama_layer import DecoderLayer
+    return DecoderLayer(w.config_dict(), ws, w.dtype, max_position or w.positions_needed(), device="cuda")
+
+
+def make_cache(layer, w: synth.Workload, tokens_per_seq: int, seqs: int, block_order_seed: int | None = None,
+               spare_blocks: int = 0):
+    from decoder_block_amd.llama_layer import PagedKVCache
+    nb = seqs * ((tokens_per_seq + 15) // 16) + spare_blocks
+    order = None
+    if block_order_seed is not None:
+        order = np.random.Generator(np.random.PCG64(block_order_seed)).permutation(nb).tolist()
+    return PagedKVCache(layer, nb, seqs, block_order=order)
+
+
+def gpu_prefill(layer, cache, x: torch.Tensor, out_dtype="f32", sids=None):
+    B = x.shape[0]
+    if sids is None:
+        sids = [cache.add_seq() for _ in range(B)]
+    out = layer.prefill(cache, sids, x.cuda(), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, sids
+
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()
