@@ -1,0 +1,235 @@
+"""Benchmark of the MI355X decoder layer (one GPU).
+
+Step = one causal prefill of the LLaMA-3-8B-shaped layer (d 4096, 32 query
+heads, 8 KV heads, I 14336, B 1, S 8192, bf16, fp32 accumulation) through the
+C ABI, on synthetic seeded inputs already resident in HBM.  The same run also
+times 128 consecutive batched decode steps of that layer (B 64, paged cache
+pre-filled at context lengths drawn from U[512, 8192]), reported under
+"decode".  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "layer prefill tokens/s + decode µs/step, LLaMA-3-8B shape; % MFMA/HBM peak"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(w) -> dict:
+    """Algorithmic flops per kernel family of one prefill (causal pairs only)."""
+    T = w.batch * w.seq_len
+    d, I, H, G, D = w.hidden_size, w.intermediate_size, w.num_attention_heads, w.num_key_value_heads, w.head_dim
+    pairs = w.batch * w.seq_len * (w.seq_len + 1) // 2
+    return {"gemm_qkv_rope": 2 * T * d * (H + 2 * G) * D,
+            "attn_prefill": 4 * D * H * pairs,
+            "gemm_o_resid": 2 * T * H * D * d,
+            "gemm_gate_up_swiglu": 4 * T * d * I,
+            "gemm_down_resid": 2 * T * I * d}
+
+
+def run_prefill(args, torch, L, synth):
+    w = synth.WORKLOADS[3]
+    log(f"[bench] prefill workload {w.name}: generating weights")
+    ws = synth.layer_weights(w)
+    layer = L.DecoderLayer(w.config_dict(), ws, "bf16", w.positions_needed())
+    del ws
+    x = synth.layer_input(w).cuda()
+    cache = L.PagedKVCache(layer, w.batch * ((w.seq_len + 15) // 16), w.batch)
+    out = torch.empty((w.batch, w.seq_len, w.hidden_size), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        sids = [cache.add_seq() for _ in range(w.batch)]
+        layer.prefill(cache, sids, x, out_dtype="bf16", out=out)
+        for s in sids:
+            cache.free_seq(s)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    L.llama_layer_profile_enable(layer.handle, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = L.llama_layer_profile_read(layer.handle, reset=True)
+    L.llama_layer_profile_enable(layer.handle, False)
+    ms = (t1 - t0) * 1e3 / args.steps
+    flops = prefill_flops(w)
+    kern = {}
+    for name, (n, tot) in prof.items():
+        avg = tot / n
+        kern[name] = {"avg_ms": round(avg, 4), "launches": n}
+        if name in flops:
+            kern[name]["tflops"] = round(flops[name] / (avg * 1e-3) / 1e12, 1)
+    dom = "gemm_gate_up_swiglu"
+    dom_ms = prof[dom][1] / prof[dom][0]
+    ach = flops[dom] / (dom_ms * 1e-3) / 1e12
+    total_flops = sum(flops.values())
+    log(f"[bench] prefill {ms:.3f} ms/step, layer {total_flops / ms / 1e9:.1f} TFLOP/s")
+    res = {
+        "tokens_per_s": w.batch * w.seq_len / (ms * 1e-3), "ms": ms, "kernels": kern,
+        "layer_tflops": total_flops / (ms * 1e-3) / 1e12,
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops[dom], "avg_launch_ms": round(dom_ms, 4)},
+    }
+    layer.close()
+    cache.close()
+    return w, res
+
+
+def run_decode(args, torch, L, synth):
+    w = synth.WORKLOADS[4]
+    log(f"[bench] decode workload {w.name}: weights and cache")
+    ws = synth.layer_weights(w)
+    layer = L.DecoderLayer(w.config_dict(), ws, "bf16", w.positions_needed())
+    del ws
+    lens = synth.context_lengths(w)
+    nsteps = args.decode_steps
+    nb = int(sum((int(l) + nsteps + args.decode_warmup + 15) // 16 for l in lens))
+    perm = synth.block_permutation(w, nb).tolist()
+    cache = L.PagedKVCache(layer, nb, w.batch, block_order=perm)
+    sids = []
+    for b in range(w.batch):
+        sid = cache.add_seq()
+        k, v = synth.cache_contents(w, b, int(lens[b]))
+        cache.write(sid, k.cuda(), v.cuda())
+        sids.append(sid)
+    xs = [synth.decode_input(w, s).cuda() for s in range(nsteps + args.decode_warmup)]
+    out = torch.empty((w.batch, w.hidden_size), dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    for s in range(args.decode_warmup):
+        layer.decode(cache, sids, xs[s], out_dtype="bf16", out=out)
+    torch.cuda.synchronize()
+    ctx_start = np.array([cache.seq_len(s) for s in sids], dtype=np.int64)
+    L.llama_layer_profile_enable(layer.handle, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(nsteps):
+        layer.decode(cache, sids, xs[args.decode_warmup + s], out_dtype="bf16", out=out)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    prof = L.llama_layer_profile_read(layer.handle, reset=True)
+    L.llama_layer_profile_enable(layer.handle, False)
+    us = (t1 - t0) * 1e6 / nsteps
+    G, D = w.num_key_value_heads, w.head_dim
+    # keys read per step: every cached key plus the new one, K and V, once per KV group
+    keys = float(np.sum(ctx_start + 1)) + w.batch * (nsteps - 1) / 2.0
+    kv_bytes = keys * G * D * 2 * 2
+    d, I, H = w.hidden_size, w.intermediate_size, w.num_attention_heads
+    weight_bytes = 2 * (d * (H + 2 * G) * D + H * D * d + 3 * d * I)
+    dom = "attn_decode_split"
+    dom_ms = prof[dom][1] / prof[dom][0]
+    ach = kv_bytes / (dom_ms * 1e-3) / 1e9
+    kern = {n: {"avg_us": round(t / c * 1e3, 2), "launches": c} for n, (c, t) in prof.items()}
+    step_bytes = kv_bytes + weight_bytes
+    log(f"[bench] decode {us:.1f} us/step, {step_bytes / (us * 1e-6) / 1e9:.0f} GB/s whole step")
+    res = {
+        "workload": w.name, "batch": w.batch, "steps": nsteps, "us_per_step": round(us, 2),
+        "mean_context": float(np.mean(ctx_start)), "kernels": kern,
+        "step_hbm_frac": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": kv_bytes, "avg_launch_ms": round(dom_ms, 4)},
+    }
+    layer.close()
+    cache.close()
+    return res
+
+
+def cpu_baseline(synth, w, n_rows: int):
+    """The float64 oracle on the prefill workload, or on a row sample of it (host cores)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    ws = synth.layer_weights(w)
+    wo = {k: synth.as_f64(v) for k, v in ws.items()}
+    x = synth.as_f64(synth.layer_input(w))
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    if n_rows >= w.seq_len:
+        t0 = time.perf_counter()
+        oracle.prefill(w.config_dict(), wo, x)
+        t = time.perf_counter() - t0
+        return {"value": round(w.batch * w.seq_len / t, 2), "unit": "tokens/s", "cores": int(threads),
+                "kind": "oracle",
+                "sample": f"{w.name}: the whole layer prefill (B {w.batch}, S {w.seq_len}) in float64, {t:.1f} s"}
+    rows = np.unique(np.linspace(0, w.seq_len - 1, n_rows).astype(np.int64))
+    t0 = time.perf_counter()
+    oracle.prefill(w.config_dict(), wo, x, rows=rows[-1:])
+    t1 = time.perf_counter()
+    oracle.prefill(w.config_dict(), wo, x, rows=rows)
+    t2 = time.perf_counter()
+    t_kv = t1 - t0                                 # K/V of all tokens + one row
+    t_full = t_kv + (t2 - t1 - t_kv) * (w.seq_len / len(rows))
+    return {"value": round(w.batch * w.seq_len / t_full, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{w.name}: K/V of all {w.seq_len} tokens plus outputs of {len(rows)} evenly spaced "
+                       f"rows, float64; {t2 - t0:.1f} s measured, full-layer time extrapolated linearly "
+                       f"in rows")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--decode-warmup", type=int, default=4)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows (>= S: the whole layer)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decoder_block_amd import llama_layer as L
+    from decoder_block_amd import synth
+    L.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    w, pre = run_prefill(args, torch, L, synth)
+    dec = None if args.no_decode else run_decode(args, torch, L, synth)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(synth, w, args.cpu_rows)
+    line = {
+        "metric": METRIC, "value": round(pre["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(pre["ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, random init)",
+        "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "hidden_size": w.hidden_size,
+                   "intermediate_size": w.intermediate_size, "num_attention_heads": w.num_attention_heads,
+                   "num_key_value_heads": w.num_key_value_heads, "rope_theta": w.rope_theta,
+                   "rms_norm_eps": w.rms_norm_eps},
+        "layer_tflops": round(pre["layer_tflops"], 1),
+        "layer_mfma_frac": round(pre["layer_tflops"] / PEAK_BF16_TFLOPS, 4),
+        "roofline": pre["roofline"],
+        "kernels": pre["kernels"],
+        "decode": dec,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

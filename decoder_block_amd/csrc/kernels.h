@@ -61,9 +61,10 @@ hipError_t launch_gemm(DType t, GemmTile tile, const GemmArgs& a, hipStream_t s)
 // RMSNorm row scale r[t] = rsqrt(mean(x[t]^2) + eps) of x [M][d] (layer dtype).
 hipError_t launch_rms_rowscale(DType t, const void* x, float* r, int M, int d, float eps,
                                hipStream_t s);
-// Second norm: r2[t] from h [M][d] fp32, plus hb = h converted to the layer dtype.
-hipError_t launch_rms_convert(DType t, const float* h, void* hb, float* r, int M, int d,
-                              float eps, hipStream_t s);
+// Second norm: r2[t] from h [M][d] fp32, plus hb = h * gamma (fp32 gamma) rounded
+// once to the layer dtype.
+hipError_t launch_rms_convert(DType t, const float* h, const float* gamma, void* hb, float* r,
+                              int M, int d, float eps, hipStream_t s);
 
 // Causal GQA prefill attention: q [B*S][H*D] -> attn [B*S][H*D], keys from the cache.
 hipError_t launch_attn_prefill(DType t, const void* q, void* attn, int H, const CacheView& c,
@@ -84,6 +85,8 @@ hipError_t launch_attn_decode_combine(DType t, const float* partial, void* attn,
 hipError_t launch_pack(DType t, const void* src, const void* gamma, void* dst, int rows,
                        int cols, int ldd, int row_mul, int row_add, hipStream_t s);
 hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s);
+// dst[i] = float(src[i]) for n elements of the layer dtype.
+hipError_t launch_to_f32(DType t, const void* src, float* dst, int n, hipStream_t s);
 
 // Small host -> device updates carried in kernel arguments: base[idx[i]] = val[i].
 constexpr int kUploadMax = 240;

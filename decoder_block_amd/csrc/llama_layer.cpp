@@ -9,8 +9,8 @@
 //   [q | k | v] = r1 * x W'qkv^T, RoPE(q, k), k/v -> cache    (W' = W diag(gamma_1))
 //   attn = causal GQA attention(q, cache)             prefill: flash; decode: split-K
 //   h = x + attn Wo^T                                  fp32 residual stream
-//   r2 = rowscale(h), hb = h in the layer dtype       RMSNorm_2 statistics
-//   s = SiLU(r2 * hb W'g^T) * (r2 * hb W'u^T)          (W' = W diag(gamma_2))
+//   r2 = rowscale(h), hb = h * gamma_2 in the layer dtype   RMSNorm_2
+//   s = SiLU(r2 * hb Wg^T) * (r2 * hb Wu^T)
 //   out = h + s Wd^T
 #include <hip/hip_runtime_api.h>
 
@@ -79,7 +79,7 @@ llama_status check_config(const llama_layer_config* c, Shape* s) {
 }
 
 struct PackedLayout {
-  size_t qkv, o, gu, down, cos, sin, total;
+  size_t qkv, o, gu, down, gamma2, cos, sin, total;
 };
 
 PackedLayout packed_layout(const Shape& s) {
@@ -93,6 +93,8 @@ PackedLayout packed_layout(const Shape& s) {
   off = align256(off + (size_t)2 * s.I_pad * s.d * s.es);
   p.down = off;
   off = align256(off + (size_t)s.d * s.I_pad * s.es);
+  p.gamma2 = off;
+  off = align256(off + (size_t)s.d * sizeof(float));
   p.cos = off;
   off = align256(off + (size_t)s.max_pos * (s.D / 2) * sizeof(float));
   p.sin = off;
@@ -385,11 +387,12 @@ llama_status llama_layer_create(const llama_layer_config* cfg, const llama_layer
   if (e == hipSuccess)
     e = llk::launch_pack(s.dt, w->v_proj, w->input_layernorm, P + L->pl.qkv, s.KD, s.d, s.d, 1, s.HD + s.KD, hs);
   if (e == hipSuccess) e = llk::launch_pack(s.dt, w->o_proj, nullptr, P + L->pl.o, s.d, s.HD, s.HD, 1, 0, hs);
-  // gate/up interleaved row by row, gamma_2 folded in
+  // gate/up interleaved row by row; gamma_2 scales the activation instead
+  // (h * gamma_2 is rounded once, the weights stay exact)
+  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->gate_proj, nullptr, P + L->pl.gu, s.I, s.d, s.d, 2, 0, hs);
+  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->up_proj, nullptr, P + L->pl.gu, s.I, s.d, s.d, 2, 1, hs);
   if (e == hipSuccess)
-    e = llk::launch_pack(s.dt, w->gate_proj, w->post_attention_layernorm, P + L->pl.gu, s.I, s.d, s.d, 2, 0, hs);
-  if (e == hipSuccess)
-    e = llk::launch_pack(s.dt, w->up_proj, w->post_attention_layernorm, P + L->pl.gu, s.I, s.d, s.d, 2, 1, hs);
+    e = llk::launch_to_f32(s.dt, w->post_attention_layernorm, reinterpret_cast<float*>(P + L->pl.gamma2), s.d, hs);
   if (e == hipSuccess) e = llk::launch_pack(s.dt, w->down_proj, nullptr, P + L->pl.down, s.d, s.I, s.I_pad, 1, 0, hs);
   if (e != hipSuccess) return fail(e);
 
@@ -692,7 +695,8 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
   HIP_TRY(timed(L, K_OPROJ, hs, [&] { return llk::launch_gemm(s.dt, tile_for(o.N), o, hs); }));
 
   // RMSNorm_2 statistics + operand copy
-  HIP_TRY(timed(L, K_RMS2, hs, [&] { return llk::launch_rms_convert(s.dt, h, hb, r2, M, s.d, eps, hs); }));
+  const float* gamma2 = reinterpret_cast<const float*>(P + L->pl.gamma2);
+  HIP_TRY(timed(L, K_RMS2, hs, [&] { return llk::launch_rms_convert(s.dt, h, gamma2, hb, r2, M, s.d, eps, hs); }));
 
   // gate/up + SiLU * up
   llk::GemmArgs g{};

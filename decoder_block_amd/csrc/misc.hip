@@ -28,6 +28,11 @@ __global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ p, size_t
   if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void to_f32_kernel(const T* __restrict__ src, float* __restrict__ dst, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) dst[i] = to_f32(src[i]);
+}
+
 __global__ __launch_bounds__(256) void upload_kernel(Upload u) {
   for (int i = threadIdx.x; i < u.n; i += 256) u.base[u.idx[i]] = u.val[i];
 }
@@ -85,6 +90,14 @@ hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s) {
   const int ntail = (int)(bytes % 16);
   zero_kernel<<<grid_for(n16), 256, 0, s>>>(reinterpret_cast<u32x4*>(dst), n16,
                                             reinterpret_cast<uint8_t*>(dst) + n16 * 16, ntail);
+  return hipGetLastError();
+}
+
+hipError_t launch_to_f32(DType t, const void* src, float* dst, int n, hipStream_t s) {
+  if (t == DType::BF16)
+    to_f32_kernel<bf16><<<grid_for(n), 256, 0, s>>>(reinterpret_cast<const bf16*>(src), dst, n);
+  else
+    to_f32_kernel<float><<<grid_for(n), 256, 0, s>>>(reinterpret_cast<const float*>(src), dst, n);
   return hipGetLastError();
 }
 

@@ -38,10 +38,12 @@ __global__ __launch_bounds__(256) void rms_rowscale_kernel(const T* __restrict__
   if (lane == 0) r[row] = 1.f / sqrtf(acc / (float)d + eps);
 }
 
-// Second norm: statistics of the fp32 residual stream h, plus h stored in the
-// layer dtype as the next GEMM's operand.
+// Second norm: statistics of the fp32 residual stream h, plus h * gamma_2
+// rounded once to the layer dtype as the next GEMM's operand (the row scale r2
+// is applied in that GEMM's epilogue).
 template <typename T>
-__global__ __launch_bounds__(256) void rms_convert_kernel(const float* __restrict__ h, T* __restrict__ hb,
+__global__ __launch_bounds__(256) void rms_convert_kernel(const float* __restrict__ h,
+                                                          const float* __restrict__ gamma, T* __restrict__ hb,
                                                           float* __restrict__ r, int M, int d, float eps) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -52,6 +54,7 @@ __global__ __launch_bounds__(256) void rms_convert_kernel(const float* __restric
   for (int c = lane * 4; c < d; c += 64 * 4) {
     f32x4 v = *reinterpret_cast<const f32x4*>(p + c);
     acc += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+    v *= *reinterpret_cast<const f32x4*>(gamma + c);
     if constexpr (sizeof(T) == 4) {
       *reinterpret_cast<f32x4*>(q + c) = v;
     } else {
@@ -74,13 +77,13 @@ hipError_t launch_rms_rowscale(DType t, const void* x, float* r, int M, int d, f
   return hipGetLastError();
 }
 
-hipError_t launch_rms_convert(DType t, const float* h, void* hb, float* r, int M, int d, float eps,
-                              hipStream_t s) {
+hipError_t launch_rms_convert(DType t, const float* h, const float* gamma, void* hb, float* r, int M, int d,
+                              float eps, hipStream_t s) {
   const int grid = (M + 3) / 4;
   if (t == DType::BF16)
-    rms_convert_kernel<bf16><<<grid, 256, 0, s>>>(h, reinterpret_cast<bf16*>(hb), r, M, d, eps);
+    rms_convert_kernel<bf16><<<grid, 256, 0, s>>>(h, gamma, reinterpret_cast<bf16*>(hb), r, M, d, eps);
   else
-    rms_convert_kernel<float><<<grid, 256, 0, s>>>(h, reinterpret_cast<float*>(hb), r, M, d, eps);
+    rms_convert_kernel<float><<<grid, 256, 0, s>>>(h, gamma, reinterpret_cast<float*>(hb), r, M, d, eps);
   return hipGetLastError();
 }
 

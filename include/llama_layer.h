@@ -114,8 +114,9 @@ llama_status llama_layer_packed_bytes(const llama_layer_config* cfg, size_t* byt
 
 /* Validate cfg, repack the weights into packed_dev (caller-owned, at least
  * llama_layer_packed_bytes, 256-byte aligned) on `stream`, build the RoPE
- * table, and return a handle.  The gammas are folded into the projection
- * weights that follow each norm (in fp32, rounded once to cfg.dtype).
+ * table, and return a handle.  gamma_1 is folded into the q/k/v weights (in
+ * fp32, rounded once to cfg.dtype); gamma_2 scales the fp32 residual stream
+ * when it is converted to the gate/up operand.
  * Synchronises `stream` before returning, so the source weights may be freed
  * afterwards.  packed_dev must outlive the handle. */
 llama_status llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights* w,

@@ -37,7 +37,7 @@ hipError_t launch_rms_rowscale(DType, const void*, float*, int, int, float, hipS
   g_log.push_back("rms1");
   return hipSuccess;
 }
-hipError_t launch_rms_convert(DType, const float*, void*, float*, int, int, float, hipStream_t) {
+hipError_t launch_rms_convert(DType, const float*, const float*, void*, float*, int, int, float, hipStream_t) {
   g_log.push_back("rms2");
   return hipSuccess;
 }
@@ -72,6 +72,10 @@ hipError_t event_elapsed_ms(float* ms, void*, void*) {
 hipError_t launch_pack(DType, const void*, const void* gamma, void*, int rows, int cols, int ldd, int row_mul,
                        int row_add, hipStream_t) {
   g_packs.push_back({rows, cols, ldd, row_mul, row_add, gamma != nullptr});
+  return hipSuccess;
+}
+hipError_t launch_to_f32(DType, const void*, float* dst, int n, hipStream_t) {
+  for (int i = 0; i < n; ++i) dst[i] = 1.0f;
   return hipSuccess;
 }
 hipError_t launch_zero(void* dst, size_t bytes, hipStream_t) {
@@ -178,8 +182,8 @@ int main() {
     CHECK(g_packs[1].rows == 128 && g_packs[1].row_add == 256 && g_packs[1].gamma);
     CHECK(g_packs[2].rows == 128 && g_packs[2].row_add == 384 && g_packs[2].gamma);
     CHECK(!g_packs[3].gamma && g_packs[3].rows == 256);
-    CHECK(g_packs[4].row_mul == 2 && g_packs[4].row_add == 0 && g_packs[4].gamma);
-    CHECK(g_packs[5].row_mul == 2 && g_packs[5].row_add == 1 && g_packs[5].gamma);
+    CHECK(g_packs[4].row_mul == 2 && g_packs[4].row_add == 0 && !g_packs[4].gamma);
+    CHECK(g_packs[5].row_mul == 2 && g_packs[5].row_add == 1 && !g_packs[5].gamma);
     CHECK(g_packs[6].cols == 688 && g_packs[6].ldd == 768 && !g_packs[6].gamma);
   }
   // the RoPE tables are the last two sections of the packed buffer

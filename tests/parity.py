@@ -13,7 +13,12 @@ from decoder_block_amd import synth
 # Tolerances, errors divided by the RMS of the oracle output ("unit-scale"):
 #   fp32 layer: max |gpu - oracle| / RMS <= 1e-4
 #   bf16 layer: max <= 3e-2 and mean <= 3e-3
-TOL = {"f32": {"max_rel": 1e-4}, "bf16": {"max_rel": 3e-2, "mean_rel": 3e-3}}
+TOL = {"f32": {"max_rel": 1e-4}, "bf16": {"max_rel": 3e-2, "mean_rel": 3e-3},
+       # gamma != 1 (a parity-only case beyond the workloads, whose gammas are 1):
+       # gamma_1 folded into W_qkv adds one bf16 rounding of the q/k/v weights,
+       # worth about 1.7e-3 in quadrature on top of the ~2.8e-3 of the gamma = 1
+       # layer at 300 tokens
+       "bf16_gamma": {"max_rel": 3e-2, "mean_rel": 4e-3}}
 
 
 def errors(gpu, ref) -> dict:

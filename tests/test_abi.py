@@ -53,7 +53,8 @@ def test_packed_bytes_cover_the_weights(L):
     n = L.llama_layer_packed_bytes(_cfg(L))
     weights = 2 * (4096 * 6144 + 4096 * 4096 + 2 * 14336 * 4096 + 4096 * 14336)
     rope = 2 * 8321 * 64 * 4
-    assert weights + rope <= n <= weights + rope + 8 * 256
+    gamma2 = 4096 * 4
+    assert weights + rope + gamma2 <= n <= weights + rope + gamma2 + 8 * 256
 
 
 @pytest.mark.parametrize("kw,status", [
