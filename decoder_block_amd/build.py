@@ -23,6 +23,9 @@ LIB = os.path.join(LIBDIR, "libllama_layer.so")
 
 ARCH = "gfx950"
 SOURCES = ["llama_layer.cpp", "gemm.hip", "norm.hip", "attn_prefill.hip", "attn_decode.hip", "misc.hip"]
+# MFMA results in VGPRs (not AGPRs): the attention kernel rescales its output
+# accumulators with VALU ops, which cannot read AGPRs.
+EXTRA = {"attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 VALU forms on this hardware
@@ -54,7 +57,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     def compile_one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *FLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         msg = _run(cmd)
         if verbose and msg.strip():
             print(msg, file=sys.stderr)

@@ -270,7 +270,6 @@ hipError_t launch_attn_decode(DType t, const void* q, float* partial, int max_sp
     if (c.D == 128) return launch_split<bf16, 128>(q, partial, max_splits, H, c, b, s);
     if (c.D == 64) return launch_split<bf16, 64>(q, partial, max_splits, H, c, b, s);
   } else {
-    if (c.D == 128) return launch_split<float, 128>(q, partial, max_splits, H, c, b, s);
     if (c.D == 64) return launch_split<float, 64>(q, partial, max_splits, H, c, b, s);
   }
   return hipErrorInvalidValue;
@@ -282,7 +281,6 @@ hipError_t launch_attn_decode_combine(DType t, const float* partial, void* attn,
     if (D == 128) return launch_combine<bf16, 128>(partial, attn, max_splits, H, b, s);
     if (D == 64) return launch_combine<bf16, 64>(partial, attn, max_splits, H, b, s);
   } else {
-    if (D == 128) return launch_combine<float, 128>(partial, attn, max_splits, H, b, s);
     if (D == 64) return launch_combine<float, 64>(partial, attn, max_splits, H, b, s);
   }
   return hipErrorInvalidValue;

@@ -7,10 +7,12 @@
 // from the paged cache, so new tokens also see every cached key before them
 // (absolute positions, "Chapter 10", section 7).
 //
-// Work split: one workgroup (4 waves, 128 query rows) per (sequence, KV
-// group, block of positions).  The 128 rows are the R = H/G query heads of
-// the group times 128/R positions, so every K/V tile staged in LDS serves all
-// heads of the group.  Row blocks are issued latest-position first (the
+// Work split: one workgroup (8 waves = 2 per SIMD, 256 query rows, 32 per
+// wave) per (sequence, KV group, block of positions).  The 256 rows are the
+// R = H/G query heads of the group times 256/R positions, so every K/V tile
+// staged in LDS serves all heads of the group.  Two waves per SIMD let one
+// wave's softmax (exp on the transcendental unit, VALU) overlap the other
+// wave's MFMAs.  Row blocks are issued latest-position first (the
 // longest causal rows start first) and the KV groups of a row block sit on
 // consecutive workgroup ids, i.e. one group per XCD.
 //
@@ -21,8 +23,9 @@
 //   O^T [D x rows]   += V_tile^T [D x keys] * P^T     (P straight from registers)
 // The cache keeps V transposed per block ([D][16 keys]), so V^T tiles are
 // staged with plain 16-byte copies.  K and V^T tiles are double buffered in
-// LDS (XOR-swizzled 16-byte chunks); the next tile's global loads are in
-// flight during the MFMAs.
+// LDS (XOR-swizzled 16-byte chunks) and moved by the gfx950 LDS DMA
+// (global_load_lds_dwordx4), so the next tile streams in during the MFMAs
+// without passing through registers.
 #include <math.h>
 
 #include "common.h"
@@ -34,29 +37,48 @@ namespace {
 template <typename T, int D_>
 struct ACfg {
   static constexpr int D = D_;
-  static constexpr int CH = Chunk<T>::N;            // elements per 16-byte chunk
-  static constexpr int KT = 64;                     // keys per tile
-  static constexpr int CPRK = D * (int)sizeof(T) / 16;  // chunks per K row
-  static constexpr int NQ = D / (2 * CH);           // QK k-steps
-  static constexpr int NDB = D / 32;                // 32-row blocks of O^T
+  static constexpr int CH = Chunk<T>::N;                 // elements per 16-byte chunk
+  static constexpr int KT = 64;                          // keys per tile
+  static constexpr int NW = 8;                           // waves per workgroup (2 per SIMD)
+  static constexpr int NT = 64 * NW;
+  static constexpr int RB = 1;                           // 32-row blocks per wave
+  static constexpr int ROWS = NW * 32 * RB;              // query rows per workgroup
+  static constexpr int CPRK = D * (int)sizeof(T) / 16;   // chunks per K (and Q) row
+  static constexpr int NQ = D / (2 * CH);                // QK k-steps
+  static constexpr int NDB = D / 32;                     // 32-row blocks of O^T
   static constexpr int VROW = KT * (int)sizeof(T) / 16;  // chunks per V^T row
-  static constexpr int LK = KT * CPRK / 256;        // K chunks loaded per thread
-  static constexpr int LV = D * VROW / 256;         // V^T chunks loaded per thread
-  static_assert(LK >= 1 && LV >= 1, "tile too small for 256 threads");
+  static constexpr int KSLOTS = KT * CPRK, VSLOTS = D * VROW;
+  static constexpr int LK = KSLOTS / NT;                 // K chunks moved per thread
+  static constexpr int LV = VSLOTS / NT;                 // V^T chunks moved per thread
+  static_assert(LK >= 1 && LV >= 1, "tile too small for the workgroup");
+  static_assert(NT == 512, "the kernel's launch bounds assume 512 threads");
 };
 
+// LDS chunk slots.  K and Q rows are CPRK chunks wide: XOR with the low bits
+// of the row spreads the 32 rows an MFMA fragment reads over all slots.  V^T
+// rows (d) are 128 or 256 bytes: XOR with d/2 keeps neighbouring row pairs in
+// different slots of a 256-byte bank window.  The swizzle is an involution
+// within a row, so the same function maps logical -> physical and back.
+template <int CPRK>
+DEVI int k_swz(int row) { return row & (CPRK - 1) & 15; }
+template <int VROW>
+DEVI int v_swz(int d) { return (d >> 1) & 7; }
+
+// Lazy rescaling: the running max of a row is only raised when a new score
+// exceeds it by more than 2^8 in exp2 units, so unnormalised P stays <= 256.
+constexpr float kRescaleLog2 = 8.f;
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__ q, T* __restrict__ attn,
+__global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__ q, T* __restrict__ attn,
                                                            int H, CacheView cache, BatchView batch) {
   using C = ACfg<T, D>;
   using vec = typename Chunk<T>::vec;
-  __shared__ u32x4 sK[2][C::KT * C::CPRK];
-  __shared__ u32x4 sV[2][D * C::VROW];
+  __shared__ u32x4 sK[2][C::KSLOTS];
+  __shared__ u32x4 sV[2][C::VSLOTS];
 
   const int G = cache.G;
   const int R = H / G;
-  const int P = 128 / R;  // positions per workgroup
+  const int P = C::ROWS / R;  // positions per workgroup
   const int S = batch.seq_len;
   const int b = blockIdx.x / G, g = blockIdx.x % G;
   const int nrb = (S + P - 1) / P;
@@ -67,17 +89,32 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
   const int HD = H * D;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hl = lane >> 5;            // lane group
-  const int j = wave * 32 + (lane & 31);  // this lane's query row in the block
-  const int r = j / P, pp = j % P;
-  const int sidx = rb * P + pp;
-  const bool active = sidx < S;
-  const int head = g * R + r;
-  const int qpos = start + (active ? sidx : rb * P);  // inactive rows mirror a valid one
-  const size_t tok = (size_t)b * S + (active ? sidx : rb * P);
+  const int hl = lane >> 5;  // lane group
 
-  // wave-uniform position range
-  int wmax = qpos, wmin = qpos;
+  // query row j of the workgroup -> (head, sequence index); rows past the end
+  // mirror the block's first row (computed, never stored)
+  auto row_head = [&](int j) { return g * R + j / P; };
+  auto row_sidx = [&](int j) {
+    const int sidx = rb * P + j % P;
+    return sidx < S ? sidx : rb * P;
+  };
+
+  const T* kpool = reinterpret_cast<const T*>(cache.k_pool);
+  const T* vpool = reinterpret_cast<const T*>(cache.v_pool);
+  const int32_t* btab = cache.block_table + (size_t)seq * cache.max_blocks;
+
+  // this lane's query rows (one per 32-row block)
+  int qpos[C::RB];
+  bool active[C::RB];
+  int wmax = 0, wmin = 1 << 30;
+#pragma unroll
+  for (int x = 0; x < C::RB; ++x) {
+    const int j = wave * 32 * C::RB + 32 * x + (lane & 31);
+    active[x] = rb * P + j % P < S;
+    qpos[x] = start + row_sidx(j);
+    wmax = max(wmax, qpos[x]);
+    wmin = min(wmin, qpos[x]);
+  }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) {
     wmax = max(wmax, __shfl_xor(wmax, m, 64));
@@ -85,200 +122,227 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(const T* __restrict__
   }
   const int last_s = min(S, (rb + 1) * P) - 1;
   const int ntiles = (start + last_s) / C::KT + 1;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
 
   // Q fragments (B operand of S^T), resident for the whole key loop
-  vec qf[C::NQ];
-  {
-    const T* qp = q + tok * HD + (size_t)head * D;
+  vec qf[C::RB][C::NQ];
 #pragma unroll
-    for (int kk = 0; kk < C::NQ; ++kk) qf[kk] = load_chunk<T>(qp + (2 * kk + hl) * C::CH);
-    if (!active) {
+  for (int x = 0; x < C::RB; ++x) {
+    const int j = wave * 32 * C::RB + 32 * x + (lane & 31);
+    const T* qp = q + ((size_t)b * S + row_sidx(j)) * HD + (size_t)row_head(j) * D;
 #pragma unroll
-      for (int kk = 0; kk < C::NQ; ++kk) qf[kk] = zero_chunk<T>();
-    }
+    for (int kk = 0; kk < C::NQ; ++kk) qf[x][kk] = load_chunk<T>(qp + (2 * kk + hl) * C::CH);
   }
 
-  const T* kpool = reinterpret_cast<const T*>(cache.k_pool);
-  const T* vpool = reinterpret_cast<const T*>(cache.v_pool);
-  const int32_t* btab = cache.block_table + (size_t)seq * cache.max_blocks;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 rk[C::LK], rv[C::LV];
-
-  auto gload = [&](int kt) {
+  // Tile kt -> LDS stage st.  Every 16-byte slot is owned by one lane: it is
+  // either filled by the LDS DMA (global_load_lds_dwordx4: lane i of a wave
+  // lands at base + 16 i) or, for keys past the end, zeroed.
+  auto issue = [&](int kt, int st) {
 #pragma unroll
     for (int i = 0; i < C::LK; ++i) {
-      const int item = tid + 256 * i;
-      const int key = item / C::CPRK, c = item % C::CPRK;
+      const int base = (wave * C::LK + i) * 64;
+      const int slot = base + lane;
+      const int key = slot / C::CPRK;
+      const int c = (slot % C::CPRK) ^ k_swz<C::CPRK>(key);
       const int kp = kt * C::KT + key;
       if (kp < kv_len) {
-        const int blk = btab[kp >> 4];
-        rk[i] = *reinterpret_cast<const u32x4*>(kpool + (((size_t)blk * G + g) * 16 + (kp & 15)) * D + c * C::CH);
+        const size_t blk = (size_t)btab[kp >> 4];
+        lds_dma16(kpool + ((blk * G + g) * 16 + (kp & 15)) * D + c * C::CH, &sK[st][base]);
       } else {
-        rk[i] = zero;
+        sK[st][slot] = zero;
       }
     }
 #pragma unroll
     for (int i = 0; i < C::LV; ++i) {
-      const int item = tid + 256 * i;
-      const int d = item / C::VROW, c = item % C::VROW;
+      const int base = (wave * C::LV + i) * 64;
+      const int slot = base + lane;
+      const int d = slot / C::VROW;
+      const int c = (slot % C::VROW) ^ v_swz<C::VROW>(d);
       const int kp = kt * C::KT + c * C::CH;  // first key of this chunk
       if (kp < kv_len) {
-        const int blk = btab[kp >> 4];
-        rv[i] = *reinterpret_cast<const u32x4*>(vpool + (((size_t)blk * G + g) * D + d) * 16 + (kp & 15));
-        if (kp + C::CH > kv_len) {  // keys past the end may hold stale data: zero them
-          vec v = __builtin_bit_cast(vec, rv[i]);
-#pragma unroll
-          for (int e = 0; e < C::CH; ++e)
-            if (kp + e >= kv_len) v[e] = from_f32<T>(0.f);
-          rv[i] = __builtin_bit_cast(u32x4, v);
-        }
+        const size_t blk = (size_t)btab[kp >> 4];
+        lds_dma16(vpool + ((blk * G + g) * D + d) * 16 + (kp & 15), &sV[st][base]);
       } else {
-        rv[i] = zero;
+        sV[st][slot] = zero;
       }
     }
   };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < C::LK; ++i) {
-      const int item = tid + 256 * i;
-      const int key = item / C::CPRK, c = item % C::CPRK;
-      sK[st][key * C::CPRK + (c ^ (key & 7))] = rk[i];
-    }
+  // After the DMA has landed: zero values of keys past the end inside a loaded
+  // chunk (they may hold stale data of another sequence).  Only the last tile.
+  auto finish = [&](int kt, int st) {
+    if ((kt + 1) * C::KT <= kv_len) return;
 #pragma unroll
     for (int i = 0; i < C::LV; ++i) {
-      const int item = tid + 256 * i;
-      const int d = item / C::VROW, c = item % C::VROW;
-      sV[st][d * C::VROW + (c ^ (d & 7))] = rv[i];
+      const int slot = (wave * C::LV + i) * 64 + lane;
+      const int d = slot / C::VROW;
+      const int c = (slot % C::VROW) ^ v_swz<C::VROW>(d);
+      const int kp = kt * C::KT + c * C::CH;
+      if (kp < kv_len && kp + C::CH > kv_len) {
+        vec v = __builtin_bit_cast(vec, sV[st][slot]);
+#pragma unroll
+        for (int e = 0; e < C::CH; ++e)
+          if (kp + e >= kv_len) v[e] = from_f32<T>(0.f);
+        sV[st][slot] = __builtin_bit_cast(u32x4, v);
+      }
     }
   };
 
   const float scale = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(D)
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x16 o[C::NDB];
+  float m_run[C::RB], l_run[C::RB];
+  f32x16 o[C::RB][C::NDB];
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
+  for (int x = 0; x < C::RB; ++x) {
+    m_run[x] = -INFINITY;
+    l_run[x] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[x][db][i] = 0.f;
+  }
 
-  gload(0);
-  sstore(0);
+  issue(0, 0);
+  wait_all_loads();
+  finish(0, 0);
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
     const int k0 = kt * C::KT;
-    if (k0 <= wmax) {
-      // ---- S^T = K Q^T ----
-      f32x16 sc[2];
+    if (kt + 1 < ntiles) issue(kt + 1, st ^ 1);  // lands while this tile computes
+    // the 64-key tile is consumed in two 32-key halves (fewer live registers)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb) {
+      const int kh = k0 + 32 * kb;
+      if (kh > wmax) continue;  // every row of this wave is before these keys
+      // ---- S^T = K Q^T: each K fragment feeds both row blocks ----
+      f32x16 sc[C::RB];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[kb][i] = 0.f;
-        const int key = 32 * kb + (lane & 31);
+      for (int x = 0; x < C::RB; ++x)
 #pragma unroll
-        for (int kk = 0; kk < C::NQ; ++kk) {
-          const int c = 2 * kk + hl;
-          const vec a = __builtin_bit_cast(vec, sK[st][key * C::CPRK + (c ^ (key & 7))]);
-          sc[kb] = mfma32_chunk(sc[kb], a, qf[kk]);
+        for (int i = 0; i < 16; ++i) sc[x][i] = 0.f;
+      const int key = 32 * kb + (lane & 31);
+#pragma unroll
+      for (int kk = 0; kk < C::NQ; ++kk) {
+        const int c = 2 * kk + hl;
+        const vec a = __builtin_bit_cast(vec, sK[st][key * C::CPRK + (c ^ k_swz<C::CPRK>(key))]);
+#pragma unroll
+        for (int x = 0; x < C::RB; ++x) sc[x] = mfma32_chunk(sc[x], a, qf[x][kk]);
+      }
+      // ---- online softmax (lane = one query row per block) ----
+      const bool need_mask = kh + 31 > wmin;
+      float mx[C::RB];
+      bool grow = false;
+#pragma unroll
+      for (int x = 0; x < C::RB; ++x) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float sv = sc[x][i];
+          if (need_mask) {
+            const int kp = kh + 8 * (i >> 2) + 4 * hl + (i & 3);
+            if (kp > qpos[x]) sv = -INFINITY;
+          }
+          sc[x][i] = sv;
+          m = fmaxf(m, sv);
+        }
+        mx[x] = fmaxf(m, __shfl_xor(m, 32, 64));
+        grow = grow || (mx[x] - m_run[x]) * scale > kRescaleLog2;
+      }
+      if (wave_any(grow)) {  // rare after the first tile
+#pragma unroll
+        for (int x = 0; x < C::RB; ++x) {
+          const float m_new = fmaxf(m_run[x], mx[x]);
+          const float alpha = fast_exp2((m_run[x] - m_new) * scale);
+          l_run[x] *= alpha;
+#pragma unroll
+          for (int db = 0; db < C::NDB; ++db) o[x][db] *= alpha;
+          m_run[x] = m_new;
         }
       }
-      // ---- online softmax (lane = one query row) ----
-      const bool need_mask = k0 + C::KT - 1 > wmin;
-      float mx = -INFINITY;
+      vec pv[C::RB][2][8 / C::CH];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float s = sc[kb][i] * scale;
-          if (need_mask) {
-            const int kp = k0 + 32 * kb + 8 * (i >> 2) + 4 * hl + (i & 3);
-            if (kp > qpos) s = -INFINITY;
-          }
-          sc[kb][i] = s;
-          mx = fmaxf(mx, s);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f(m_run - m_new);
-      float psum = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int x = 0; x < C::RB; ++x) {
+        const float msc = m_run[x] * scale;
+        float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float p = exp2f(sc[kb][i] - m_new);
-          sc[kb][i] = p;
+          const float p = fast_exp2(fmaf(sc[x][i], scale, -msc));
           psum += p;
+          pv[x][i >> 3][(i & 7) / C::CH][(i & 7) % C::CH] = from_f32<T>(p);
         }
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+        l_run[x] += psum;
+      }
 
-      // ---- O^T += V^T P^T ----
+      // ---- O^T += V^T P^T: each V^T fragment feeds both row blocks ----
       // A operand: lane (row d, group hl) supplies keys 16m+4hl+{0..3} and
       // 16m+8+4hl+{0..3}, matching the keys its P registers hold.
       const char* vb = reinterpret_cast<const char*>(&sV[st][0]);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int m = 0; m < 2; ++m) {
+        const int kA = 32 * kb + 16 * m + 4 * hl, kB = kA + 8;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          vec pv[8 / C::CH];
+        for (int db = 0; db < C::NDB; ++db) {
+          const int d = 32 * db + (lane & 31);
+          auto piece = [&](int kk2) {  // 4 consecutive keys of row d
+            const int byte = kk2 * (int)sizeof(T);
+            return vb + (size_t)(d * C::VROW + ((byte >> 4) ^ v_swz<C::VROW>(d))) * 16 + (byte & 15);
+          };
+          if constexpr (sizeof(T) == 2) {
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(piece(kA));
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(piece(kB));
+            const vec a = __builtin_bit_cast(vec, u32x4{lo[0], lo[1], hi[0], hi[1]});
 #pragma unroll
-          for (int e = 0; e < 8; ++e) pv[e / C::CH][e % C::CH] = from_f32<T>(sc[kb][8 * m + e]);
+            for (int x = 0; x < C::RB; ++x) o[x][db] = mfma32_chunk(o[x][db], a, pv[x][m][0]);
+          } else {
+            const vec a0 = *reinterpret_cast<const vec*>(piece(kA));
+            const vec a1 = *reinterpret_cast<const vec*>(piece(kB));
 #pragma unroll
-          for (int db = 0; db < C::NDB; ++db) {
-            const int d = 32 * db + (lane & 31);
-            const char* row = vb + (size_t)d * C::VROW * 16;
-            auto piece = [&](int key) {  // 4 consecutive keys of row d
-              const int byte = key * (int)sizeof(T);
-              return row + (((byte >> 4) ^ (d & 7)) << 4) + (byte & 15);
-            };
-            const int kA = 32 * kb + 16 * m + 4 * hl, kB = kA + 8;
-            if constexpr (sizeof(T) == 2) {
-              const u32x2 lo = *reinterpret_cast<const u32x2*>(piece(kA));
-              const u32x2 hi = *reinterpret_cast<const u32x2*>(piece(kB));
-              const vec a = __builtin_bit_cast(vec, u32x4{lo[0], lo[1], hi[0], hi[1]});
-              o[db] = mfma32_chunk(o[db], a, pv[0]);
-            } else {
-              const vec a0 = *reinterpret_cast<const vec*>(piece(kA));
-              const vec a1 = *reinterpret_cast<const vec*>(piece(kB));
-              o[db] = mfma32_chunk(o[db], a0, pv[0]);
-              o[db] = mfma32_chunk(o[db], a1, pv[8 / C::CH - 1]);
+            for (int x = 0; x < C::RB; ++x) {
+              o[x][db] = mfma32_chunk(o[x][db], a0, pv[x][m][0]);
+              o[x][db] = mfma32_chunk(o[x][db], a1, pv[x][m][8 / C::CH - 1]);
             }
           }
         }
+      }
     }
-    if (kt + 1 < ntiles) sstore(st ^ 1);
+    if (kt + 1 < ntiles) {
+      wait_all_loads();
+      finish(kt + 1, st ^ 1);
+    }
     __syncthreads();
   }
 
-  if (!active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const float inv = 1.f / l_tot;
-  T* op = attn + tok * HD + (size_t)head * D;
 #pragma unroll
-  for (int db = 0; db < C::NDB; ++db)
+  for (int x = 0; x < C::RB; ++x) {
+    if (!active[x]) continue;
+    const int j = wave * 32 * C::RB + 32 * x + (lane & 31);
+    const float l_tot = l_run[x] + __shfl_xor(l_run[x], 32, 64);
+    const float inv = 1.f / l_tot;
+    T* op = attn + ((size_t)b * S + row_sidx(j)) * HD + (size_t)row_head(j) * D;
 #pragma unroll
-    for (int ig = 0; ig < 4; ++ig) {
-      const int d0 = 32 * db + 8 * ig + 4 * hl;
-      if constexpr (sizeof(T) == 2) {
-        *reinterpret_cast<bf16x4*>(op + d0) =
-            bf16x4{from_f32<bf16>(o[db][4 * ig] * inv), from_f32<bf16>(o[db][4 * ig + 1] * inv),
-                   from_f32<bf16>(o[db][4 * ig + 2] * inv), from_f32<bf16>(o[db][4 * ig + 3] * inv)};
-      } else {
-        *reinterpret_cast<f32x4*>(op + d0) =
-            f32x4{o[db][4 * ig] * inv, o[db][4 * ig + 1] * inv, o[db][4 * ig + 2] * inv, o[db][4 * ig + 3] * inv};
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int ig = 0; ig < 4; ++ig) {
+        const int d0 = 32 * db + 8 * ig + 4 * hl;
+        const f32x16& ov = o[x][db];
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<bf16x4*>(op + d0) =
+              bf16x4{from_f32<bf16>(ov[4 * ig] * inv), from_f32<bf16>(ov[4 * ig + 1] * inv),
+                     from_f32<bf16>(ov[4 * ig + 2] * inv), from_f32<bf16>(ov[4 * ig + 3] * inv)};
+        } else {
+          *reinterpret_cast<f32x4*>(op + d0) =
+              f32x4{ov[4 * ig] * inv, ov[4 * ig + 1] * inv, ov[4 * ig + 2] * inv, ov[4 * ig + 3] * inv};
+        }
       }
-    }
+  }
 }
 
 template <typename T, int D>
 hipError_t launch_d(const void* q, void* attn, int H, const CacheView& c, const BatchView& b, hipStream_t s) {
   const int R = H / c.G;
-  const int P = 128 / R;
+  const int P = ACfg<T, D>::ROWS / R;
   dim3 grid(c.G * b.batch, (b.seq_len + P - 1) / P);
-  attn_prefill_kernel<T, D><<<grid, 256, 0, s>>>(reinterpret_cast<const T*>(q), reinterpret_cast<T*>(attn), H, c, b);
+  attn_prefill_kernel<T, D><<<grid, ACfg<T, D>::NT, 0, s>>>(reinterpret_cast<const T*>(q), reinterpret_cast<T*>(attn), H, c, b);
   return hipGetLastError();
 }
 
@@ -286,12 +350,11 @@ hipError_t launch_d(const void* q, void* attn, int H, const CacheView& c, const 
 
 hipError_t launch_attn_prefill(DType t, const void* q, void* attn, int H, const CacheView& c, const BatchView& b,
                                hipStream_t s) {
-  if (H % c.G != 0 || 128 % (H / c.G) != 0) return hipErrorInvalidValue;
+  if (H % c.G != 0 || 64 % (H / c.G) != 0) return hipErrorInvalidValue;
   if (t == DType::BF16) {
     if (c.D == 128) return launch_d<bf16, 128>(q, attn, H, c, b, s);
     if (c.D == 64) return launch_d<bf16, 64>(q, attn, H, c, b, s);
   } else {
-    if (c.D == 128) return launch_d<float, 128>(q, attn, H, c, b, s);
     if (c.D == 64) return launch_d<float, 64>(q, attn, H, c, b, s);
   }
   return hipErrorInvalidValue;

@@ -91,6 +91,16 @@ DEVI f32x16 mfma32_chunk(f32x16 c, f32x4 a, f32x4 b) {
 
 DEVI int lane_id() { return __lane_id(); }
 
+// gfx950 device builtins, wrapped in plain device functions so that kernel
+// templates using them still get their host-side launch stubs.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// LDS DMA: each lane's 16 bytes at g land at lds_base + 16 * lane (lds_base wave-uniform).
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
+__device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
+
 // Exchange with lane l ^ m within a wave (m < 64).
 DEVI float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 

@@ -56,6 +56,7 @@ llama_status check_config(const llama_layer_config* c, Shape* s) {
   const int D = c->hidden_size / c->num_attention_heads;
   if (D % 2 != 0) return LLAMA_ERR_SHAPE;  // RoPE pairs need an even head_dim ("Chapter 10", section 3)
   if (D != 64 && D != 128) return LLAMA_ERR_UNSUPPORTED;
+  if (c->dtype == LLAMA_DTYPE_F32 && D != 64) return LLAMA_ERR_UNSUPPORTED;
   const int R = c->num_attention_heads / c->num_key_value_heads;
   if (R > 16 || (R & (R - 1)) != 0) return LLAMA_ERR_UNSUPPORTED;
   if (c->hidden_size % 64 != 0 || c->intermediate_size % 8 != 0) return LLAMA_ERR_SHAPE;

@@ -81,7 +81,8 @@ typedef enum { LLAMA_DTYPE_F32 = 0, LLAMA_DTYPE_BF16 = 1 } llama_dtype;
 
 /* The config.json fields of the layer ("Chapter 10", section 1) plus the
  * storage dtype and the RoPE table length.  Accumulation is always fp32.
- * Supported: head_dim D = hidden_size / num_attention_heads in {64, 128},
+ * Supported: head_dim D = hidden_size / num_attention_heads in {64, 128}
+ * (fp32 layers: 64),
  * num_attention_heads / num_key_value_heads in {1, 2, 4, 8, 16},
  * hidden_size a multiple of 64, intermediate_size a multiple of 8. */
 typedef struct {
