@@ -134,10 +134,23 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
     for (int kk = 0; kk < C::NQ; ++kk) qf[x][kk] = load_chunk<T>(qp + (2 * kk + hl) * C::CH);
   }
 
+  // Physical block ids of a tile's four 16-key blocks, fetched one tile ahead
+  // so that the DMA addresses never wait on a fresh block-table load.
+  static_assert(C::KT == 64, "four 16-key blocks per tile");
+  typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
+  auto fetch_blocks = [&](int kt) {
+    const int last = cache.max_blocks - 1;
+    return i32x4v{btab[min(kt * 4 + 0, last)], btab[min(kt * 4 + 1, last)], btab[min(kt * 4 + 2, last)],
+                  btab[min(kt * 4 + 3, last)]};
+  };
+  auto pick = [&](i32x4v blk, int u) {  // blk[u] with a lane-varying u, without dynamic indexing
+    return u == 0 ? blk[0] : u == 1 ? blk[1] : u == 2 ? blk[2] : blk[3];
+  };
+
   // Tile kt -> LDS stage st.  Every 16-byte slot is owned by one lane: it is
   // either filled by the LDS DMA (global_load_lds_dwordx4: lane i of a wave
   // lands at base + 16 i) or, for keys past the end, zeroed.
-  auto issue = [&](int kt, int st) {
+  auto issue = [&](int kt, int st, i32x4v blk) {
 #pragma unroll
     for (int i = 0; i < C::LK; ++i) {
       const int base = (wave * C::LK + i) * 64;
@@ -146,8 +159,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
       const int c = (slot % C::CPRK) ^ k_swz<C::CPRK>(key);
       const int kp = kt * C::KT + key;
       if (kp < kv_len) {
-        const size_t blk = (size_t)btab[kp >> 4];
-        lds_dma16(kpool + ((blk * G + g) * 16 + (kp & 15)) * D + c * C::CH, &sK[st][base]);
+        const size_t bk = (size_t)pick(blk, key >> 4);
+        lds_dma16(kpool + ((bk * G + g) * 16 + (kp & 15)) * D + c * C::CH, &sK[st][base]);
       } else {
         sK[st][slot] = zero;
       }
@@ -160,8 +173,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
       const int c = (slot % C::VROW) ^ v_swz<C::VROW>(d);
       const int kp = kt * C::KT + c * C::CH;  // first key of this chunk
       if (kp < kv_len) {
-        const size_t blk = (size_t)btab[kp >> 4];
-        lds_dma16(vpool + ((blk * G + g) * D + d) * 16 + (kp & 15), &sV[st][base]);
+        const size_t bk = (size_t)pick(blk, (c * C::CH) >> 4);
+        lds_dma16(vpool + ((bk * G + g) * D + d) * 16 + (kp & 15), &sV[st][base]);
       } else {
         sV[st][slot] = zero;
       }
@@ -200,7 +213,9 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
       for (int i = 0; i < 16; ++i) o[x][db][i] = 0.f;
   }
 
-  issue(0, 0);
+  i32x4v blk_next = fetch_blocks(0);
+  issue(0, 0, blk_next);
+  blk_next = fetch_blocks(1);
   wait_all_loads();
   finish(0, 0);
   __syncthreads();
@@ -208,7 +223,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
   for (int kt = 0; kt < ntiles; ++kt) {
     const int st = kt & 1;
     const int k0 = kt * C::KT;
-    if (kt + 1 < ntiles) issue(kt + 1, st ^ 1);  // lands while this tile computes
+    if (kt + 1 < ntiles) {
+      issue(kt + 1, st ^ 1, blk_next);  // lands while this tile computes
+      blk_next = fetch_blocks(kt + 2);
+    }
     // the 64-key tile is consumed in two 32-key halves (fewer live registers)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
