@@ -88,7 +88,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
   const int kv_len = start + S;
   const int HD = H * D;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int hl = lane >> 5;  // lane group
 
   // query row j of the workgroup -> (head, sequence index); rows past the end

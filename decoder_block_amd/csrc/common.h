@@ -94,11 +94,54 @@ DEVI int lane_id() { return __lane_id(); }
 // gfx950 device builtins, wrapped in plain device functions so that kernel
 // templates using them still get their host-side launch stubs.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 // LDS DMA: each lane's 16 bytes at g land at lds_base + 16 * lane (lds_base wave-uniform).
 __device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
   __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
 }
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
+// Workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations, not for its outstanding global loads / LDS DMAs (which
+// __syncthreads would drain).  The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait until at most N vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and [15:14], expcnt and lgkmcnt
+// left at their maxima, i.e. not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Buffer resource (V#) of a raw byte buffer: base address, num_records in
+// bytes (loads at offsets past it return zero), gfx9 raw-buffer flags.
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+DEVI i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int32_t)(uint32_t)a, (int32_t)(uint32_t)(a >> 32), (int32_t)bytes, 0x00020000};
+}
+__device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds,
+                                                int size, int voffset, int soffset, int offset,
+                                                int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
+// Buffer LDS DMA: lane i's 16 bytes at (rsrc base + voffset) land at lds_base + 16 i.
+__device__ __forceinline__ void buf_dma16(i32x4 rsrc, void* lds_base, int voffset) {
+  llvm_amdgcn_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)(lds_base), 16, voffset, 0,
+                                  0, 0);
+}
+// The same DMA written as inline assembly.  The compiler then does not know
+// that it writes LDS, so it never makes an LDS read wait for it (it cannot
+// always tell slots of a ring apart and would otherwise drain every
+// outstanding DMA before each read): the caller orders LDS itself, with
+// wait_vmcnt and a barrier between a stage's DMAs and the reads of that stage.
+// lds_base must be wave-uniform.
+__device__ __forceinline__ void buf_dma16_async(i32x4 rsrc, const void* lds_base, int voffset) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
 __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 
 // Exchange with lane l ^ m within a wave (m < 64).

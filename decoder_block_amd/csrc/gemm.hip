@@ -17,13 +17,17 @@
 //             registers  ("3.2 Core components", 3.2.2);
 //   RESID_OUT out = h + s W_down^T  ("LLaMA3 Block", 4.2 step 8).
 //
-// Tiles: BN features x BM tokens per workgroup, K staged 128 bytes per row
-// (64 bf16 / 32 fp32) through a double-buffered LDS ring with an XOR swizzle
-// of the 16-byte chunk index, global loads for stage k+1 in flight while
-// stage k feeds the MFMAs.  The workgroup -> tile map keeps the tiles that
-// share weight panels on one XCD (8 XCDs, each with its own L2).
+// Tiles: BN features x BM tokens per workgroup, K staged 64 bytes per row
+// (32 bf16 / 16 fp32) through a 4-deep LDS ring with an XOR swizzle of the
+// 16-byte chunk index.  Stages are moved by the buffer LDS DMA (buffer_load
+// ... lds, no register staging) three stages ahead of the MFMAs; each stage
+// waits only for its own DMAs (s_waitcnt vmcnt) and one barrier, and LDS
+// reads never wait for the DMAs of other stages.  The workgroup -> tile map
+// keeps the tiles that share weight panels on one XCD (8 XCDs, each with its
+// own L2).
 #include "common.h"
 #include "kernels.h"
+#include <type_traits>
 
 namespace llk {
 namespace {
@@ -32,19 +36,22 @@ template <typename T, int BN_, int BM_, int WN_, int WM_>
 struct Cfg {
   static constexpr int BN = BN_, BM = BM_, WN = WN_, WM = WM_;
   static constexpr int NT = 64 * WN * WM;
-  static constexpr int CPR = 8;  // 16-byte chunks per tile row
+  static constexpr int CPR = 4;     // 16-byte chunks per tile row and stage (64 bytes of K)
+  static constexpr int NSTAGE = 4;  // LDS ring depth
   static constexpr int BK = CPR * Chunk<T>::N;
   static constexpr int FW = BN / WN, TW = BM / WM;
   static constexpr int FI = FW / 16, TJ = TW / 16;
-  static constexpr int RSTEP = NT / CPR;  // tile rows covered by one pass of the threads
-  static constexpr int LW = BN / RSTEP, LX = BM / RSTEP;
-  static_assert(BN % RSTEP == 0 && BM % RSTEP == 0, "tile rows must split evenly");
+  static constexpr int LW = BN * CPR / NT, LX = BM * CPR / NT;  // 16-byte DMAs per thread per stage
+  static_assert(LW * NT == BN * CPR && LX * NT == BM * CPR && LW >= 1 && LX >= 1, "tile must split evenly");
   static_assert(FW % 16 == 0 && TW % 16 == 0, "wave tile must be 16-aligned");
 };
 
-DEVI int swz(int row, int c) { return row * 8 + (c ^ (row & 7)); }
+// 16-byte slot of (row, chunk) in a stage: XOR with row/4 spreads the 16 rows
+// a fragment reads over all four slots of each 64-byte row group.
+DEVI int swz(int row, int c) { return row * 4 + (c ^ ((row >> 2) & 3)); }
 
-DEVI float silu(float z) { return z / (1.f + __expf(-z)); }
+// z * sigmoid(z) with the hardware exp2 and reciprocal (about 1 ulp each)
+DEVI float silu(float z) { return z * fast_rcp(1.f + fast_exp2(-1.4426950408889634f * z)); }
 
 template <typename T>
 DEVI void store4(T* p, float a, float b, float c, float d) {
@@ -133,8 +140,16 @@ DEVI void epilogue(const GemmArgs& a, int t, int f, f32x4 v) {
 template <typename T, typename C, int EPI>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   using vec = typename Chunk<T>::vec;
-  __shared__ u32x4 sW[2][C::BN * C::CPR];
-  __shared__ u32x4 sX[2][C::BM * C::CPR];
+  // One LDS array per ring slot (the slot's W rows, then its X rows).  With
+  // distinct arrays the compiler can tell that a fragment read of one slot
+  // does not depend on DMAs still landing in the others, and so does not
+  // drain them before the read.
+  static_assert(C::NSTAGE == 4, "four ring slots");
+  constexpr int SLOT = (C::BN + C::BM) * C::CPR;
+  __shared__ u32x4 L0[SLOT];
+  __shared__ u32x4 L1[SLOT];
+  __shared__ u32x4 L2[SLOT];
+  __shared__ u32x4 L3[SLOT];
 
   // ---- workgroup -> tile: XCD-contiguous ranges, then grouped along M ----
   const int tiles_n = a.N / C::BN;
@@ -152,34 +167,56 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   const int n0 = tn * C::BN, m0 = tm * C::BM;
 
   const int tid = threadIdx.x;
-  const int lc = tid & 7, lr = tid >> 3;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wn = wave % C::WN, wm = wave / C::WN;
 
-  const T* W = reinterpret_cast<const T*>(a.W);
-  const T* X = reinterpret_cast<const T*>(a.X);
-  u32x4 rw[C::LW], rx[C::LX];
-  const u32x4 zero = {0u, 0u, 0u, 0u};
+  // Global -> LDS by buffer DMA: lane i of a wave fills slot base + i.  Slot s
+  // of a stage holds logical chunk (s % 4) ^ swizzle(row) of row s / 4, so the
+  // lane loads exactly that chunk (the swizzle is its own inverse).  Rows of X
+  // past M fall outside the buffer's range and arrive as zeros.
+  constexpr int ES = (int)sizeof(T);
+  int vW[C::LW], vX[C::LX];
+#pragma unroll
+  for (int i = 0; i < C::LW; ++i) {
+    const int slot = (wave * C::LW + i) * 64 + lane;
+    const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
+    vW[i] = (row * a.K + c * Chunk<T>::N) * ES;
+  }
+#pragma unroll
+  for (int i = 0; i < C::LX; ++i) {
+    const int slot = (wave * C::LX + i) * 64 + lane;
+    const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
+    vX[i] = (row * a.ldx + c * Chunk<T>::N) * ES;
+  }
+  const char* Wt = reinterpret_cast<const char*>(a.W) + (size_t)n0 * a.K * ES;
+  const char* Xt = reinterpret_cast<const char*>(a.X) + (size_t)m0 * a.ldx * ES;
+  // bytes of X from the tile's first row to the end of the matrix (< 2^31 for
+  // every supported shape), kept wave-uniform so the descriptor lives in SGPRs
+  const uint64_t xb = (uint64_t)(a.M - m0) * (uint64_t)a.ldx * ES;
+  const int x_bytes = __builtin_amdgcn_readfirstlane((int)(xb < 0x7fffffffull ? xb : 0x7fffffffull));
+  const int nk = a.K / C::BK;
 
-  auto gload = [&](int kt) {
-    const int kel = kt * C::BK + lc * Chunk<T>::N;
-#pragma unroll
-    for (int i = 0; i < C::LW; ++i) {
-      const int row = lr + i * C::RSTEP;
-      rw[i] = *reinterpret_cast<const u32x4*>(W + (size_t)(n0 + row) * a.K + kel);
-    }
-#pragma unroll
-    for (int i = 0; i < C::LX; ++i) {
-      const int m = m0 + lr + i * C::RSTEP;
-      rx[i] = m < a.M ? *reinterpret_cast<const u32x4*>(X + (size_t)m * a.ldx + kel) : zero;
-    }
+  auto slot_of = [&](auto s_) -> u32x4* {
+    constexpr int S = decltype(s_)::value & 3;
+    if constexpr (S == 0) return L0;
+    else if constexpr (S == 1) return L1;
+    else if constexpr (S == 2) return L2;
+    else return L3;
   };
-  auto sstore = [&](int st) {
+  // Stages past the end are issued against an empty buffer (zero records):
+  // they move no memory but keep the DMA count per stage uniform, so every
+  // stage waits with the same count.
+  auto issue = [&](int kt, u32x4* L) {
+    const bool live = kt < nk;
+    const int kb = live ? kt * C::BK * ES : 0;
+    const i32x4 rW = make_rsrc(Wt + kb, live ? 0x7fffffffu : 0u);
+    const i32x4 rX = make_rsrc(Xt + kb, live ? (uint32_t)(x_bytes - kb) : 0u);
 #pragma unroll
-    for (int i = 0; i < C::LW; ++i) sW[st][swz(lr + i * C::RSTEP, lc)] = rw[i];
+    for (int i = 0; i < C::LW; ++i) buf_dma16_async(rW, L + (wave * C::LW + i) * 64, vW[i]);
 #pragma unroll
-    for (int i = 0; i < C::LX; ++i) sX[st][swz(lr + i * C::RSTEP, lc)] = rx[i];
+    for (int i = 0; i < C::LX; ++i) buf_dma16_async(rX, L + C::BN * C::CPR + (wave * C::LX + i) * 64, vX[i]);
   };
+  constexpr int PER = C::LW + C::LX;  // DMAs per thread per stage
 
   f32x4 acc[C::FI][C::TJ];
 #pragma unroll
@@ -187,37 +224,49 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < C::TJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = a.K / C::BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-
   const int l16 = lane & 15, lg = lane >> 4;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  // Stage kt in ring slot kt & 3: it has landed once at most this wave's DMAs
+  // of stages kt+1 and kt+2 are outstanding; after the barrier every wave's
+  // part is in LDS and every wave is done with stage kt-1, whose slot takes
+  // stage kt+3.  One 32-deep k-step per stage: lane group lg reads chunk lg.
+  auto stage = [&](int kt, auto s_) {
+    using S = decltype(s_);
+    wait_vmcnt<2 * PER>();
+    lds_barrier();
+    issue(kt + 3, slot_of(std::integral_constant<int, S::value + 3>{}));
+    const u32x4* L = slot_of(s_);
+    vec af[C::FI], bf[C::TJ];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = ks * 4 + lg;
-      vec af[C::FI], bf[C::TJ];
+    for (int i = 0; i < C::FI; ++i) af[i] = __builtin_bit_cast(vec, L[swz(wn * C::FW + 16 * i + l16, lg)]);
 #pragma unroll
-      for (int i = 0; i < C::FI; ++i) {
-        const int row = wn * C::FW + 16 * i + l16;
-        af[i] = __builtin_bit_cast(vec, sW[st][swz(row, c)]);
-      }
+    for (int j = 0; j < C::TJ; ++j)
+      bf[j] = __builtin_bit_cast(vec, L[C::BN * C::CPR + swz(wm * C::TW + 16 * j + l16, lg)]);
 #pragma unroll
-      for (int j = 0; j < C::TJ; ++j) {
-        const int row = wm * C::TW + 16 * j + l16;
-        bf[j] = __builtin_bit_cast(vec, sX[st][swz(row, c)]);
-      }
+    for (int i = 0; i < C::FI; ++i)
 #pragma unroll
-      for (int i = 0; i < C::FI; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TJ; ++j) acc[i][j] = mfma16_chunk(acc[i][j], af[i], bf[j]);
-    }
-    if (kt + 1 < nk) sstore(st ^ 1);
-    __syncthreads();
+      for (int j = 0; j < C::TJ; ++j) acc[i][j] = mfma16_chunk(acc[i][j], af[i], bf[j]);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  issue(0, L0);
+  issue(1, L1);
+  issue(2, L2);
+  int kt = 0;
+  for (; kt + 4 <= nk; kt += 4) {
+    stage(kt, I0{});
+    stage(kt + 1, I1{});
+    stage(kt + 2, I2{});
+    stage(kt + 3, I3{});
   }
+  // K is a multiple of 2 * BK, so at most two stages remain (slots 0 and 1)
+  if (kt < nk) {
+    stage(kt, I0{});
+    stage(kt + 1, I1{});
+  }
+  wait_vmcnt<0>();  // the (empty) DMAs issued past the end have retired
 
 #pragma unroll
   for (int i = 0; i < C::FI; ++i) {
@@ -232,7 +281,11 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
 
 template <typename T, typename C>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
-  if (a.N % C::BN != 0 || a.K % C::BK != 0 || a.M <= 0) return hipErrorInvalidValue;
+  if (a.N % C::BN != 0 || a.K % (2 * C::BK) != 0 || a.M <= 0) return hipErrorInvalidValue;
+  // 32-bit buffer offsets: a tile's rows times the row pitch must stay below 2^31
+  if ((int64_t)C::BN * a.K * (int64_t)sizeof(T) >= (1ll << 31) ||
+      (int64_t)C::BM * a.ldx * (int64_t)sizeof(T) >= (1ll << 31))
+    return hipErrorInvalidValue;
   const int grid = (a.N / C::BN) * ((a.M + C::BM - 1) / C::BM);
   switch (a.epi) {
     case Epi::QKV: gemm_kernel<T, C, 0><<<grid, C::NT, 0, s>>>(a); break;
