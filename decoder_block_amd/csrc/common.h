@@ -104,7 +104,12 @@ __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0)
 // operations, not for its outstanding global loads / LDS DMAs (which
 // __syncthreads would drain).  The memory clobber keeps the compiler from
 // moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The LDS wait is the compiler's own s_waitcnt (0xC07F: lgkmcnt 0, vmcnt and
+// expcnt at their maxima), so its wait bookkeeping knows those reads are done.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and [15:14], expcnt and lgkmcnt
@@ -130,17 +135,22 @@ __device__ __forceinline__ void buf_dma16(i32x4 rsrc, void* lds_base, int voffse
   llvm_amdgcn_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)(lds_base), 16, voffset, 0,
                                   0, 0);
 }
-// The same DMA written as inline assembly.  The compiler then does not know
-// that it writes LDS, so it never makes an LDS read wait for it (it cannot
-// always tell slots of a ring apart and would otherwise drain every
-// outstanding DMA before each read): the caller orders LDS itself, with
-// wait_vmcnt and a barrier between a stage's DMAs and the reads of that stage.
-// lds_base must be wave-uniform.
-__device__ __forceinline__ void buf_dma16_async(i32x4 rsrc, const void* lds_base, int voffset) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v), "v"(voffset), "s"(rsrc)
+// LDS byte address of a __shared__ object (wave-uniform).
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+// The same DMA written as inline assembly, to the LDS byte address lds (an
+// SGPR value).  The compiler then does not know that it writes LDS, so it
+// never makes an LDS read wait for it (it cannot always tell slots of a ring
+// apart and would otherwise drain every outstanding DMA before each read):
+// the caller orders LDS itself, with wait_vmcnt and a barrier between a
+// stage's DMAs and the reads of that stage.
+__device__ __forceinline__ void buf_dma16_to(i32x4 rsrc, uint32_t lds, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
+}
+__device__ __forceinline__ void buf_dma16_async(i32x4 rsrc, const void* lds_base, int voffset) {
+  buf_dma16_to(rsrc, lds_address(lds_base), voffset);
 }
 __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 
