@@ -23,9 +23,10 @@ LIB = os.path.join(LIBDIR, "libllama_layer.so")
 
 ARCH = "gfx950"
 SOURCES = ["llama_layer.cpp", "gemm.hip", "norm.hip", "attn_prefill.hip", "attn_decode.hip", "misc.hip"]
-# MFMA results in VGPRs (not AGPRs): the attention kernel rescales its output
+# MFMA results in VGPRs (not AGPRs): the attention kernels rescale their output
 # accumulators with VALU ops, which cannot read AGPRs.
-EXTRA = {"attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+         "attn_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 VALU forms on this hardware

@@ -215,6 +215,171 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 split kernel.  A workgroup takes one (sequence, group, chunk of 1024
+// keys); each of its four waves walks its own quarter (256 keys = 16 cache
+// blocks) and the quarters are merged through LDS at the end.  Per 16-key
+// block:
+//   S^T [16 keys x heads] = K_block [16 x D] * Q^T     (16x16x32 MFMAs)
+//   O^T [D x heads]      += V_block^T [D x 16] * P^T   (16x16x16 MFMAs)
+// The score layout (lane: head column, four consecutive keys) is exactly the
+// B operand layout of the second product, so P never leaves the lane.  The
+// K and V blocks of block i+1 are loaded while block i is computed (two
+// register buffers).  Short per-wave ranges keep the waves' work even, and
+// the small register footprint keeps several waves per SIMD in flight.
+// ---------------------------------------------------------------------------
+constexpr int kWaveKeys = kChunkKeys / 4;
+
+template <int D>
+struct KV16 {
+  bf16x8 k[D / 32];   // K rows: lane (key c16, k-group g4) holds D-chunks 4s + g4
+  u32x2 v[D / 16];    // V^T rows 16 db + c16, keys 4 g4 .. 4 g4 + 3
+};
+
+// Loads of block blk (group g) through buffer descriptors; a block that is not
+// live gets an empty descriptor, so the load moves no memory and returns zeros
+// while keeping every iteration's load count the same.
+template <int D>
+DEVI void load_kv16(KV16<D>& r, const bf16* kpool, const bf16* vpool, int blk, bool live, int G, int g, int c16,
+                    int g4) {
+  constexpr uint32_t kBytes = 16 * D * 2;
+  const size_t off = ((size_t)blk * G + g) * 16 * D;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kpool + off), 0, live ? kBytes : 0u, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(vpool + off), 0, live ? kBytes : 0u, 0x00020000);
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+    r.k[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, (c16 * D + (4 * s + g4) * 8) * 2, 0, 0));
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+    r.v[db] = __builtin_amdgcn_raw_buffer_load_b64(rv, ((16 * db + c16) * 16 + 4 * g4) * 2, 0, 0);
+}
+
+DEVI f32x4 mfma16x16x16(f32x4 c, u32x2 a, u32x2 b) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0,
+                                                    0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 3) void attn_decode_wave_kernel(const bf16* __restrict__ q, float* __restrict__ part,
+                                                               int max_splits, int H, CacheView cache,
+                                                               BatchView batch) {
+  __shared__ float sm[4][16][D + 2];
+  const int G = cache.G;
+  const int R = H / G;
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const int split = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int seq = batch.desc[2 * b];
+  const int kv_len = batch.desc[2 * b + 1] + 1;
+  if (split * kChunkKeys >= kv_len) return;
+  const int k_begin = split * kChunkKeys + wave * kWaveKeys;
+  const int nkeys = max(0, min(kv_len - k_begin, kWaveKeys));
+  const int nblk = (nkeys + 15) >> 4;
+
+  const int c16 = lane & 15, g4 = lane >> 4;
+  bf16x8 qf[D / 32];
+  {
+    const bf16* qp = q + (size_t)b * H * D + (size_t)(g * R + c16) * D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) qf[s] = c16 < R ? load_chunk<bf16>(qp + (4 * s + g4) * 8) : zero_chunk<bf16>();
+  }
+  const int32_t* btab = cache.block_table + (size_t)seq * cache.max_blocks + (k_begin >> 4);
+  const bf16* kpool = reinterpret_cast<const bf16*>(cache.k_pool);
+  const bf16* vpool = reinterpret_cast<const bf16*>(cache.v_pool);
+
+  const float scale = 1.4426950408889634f / sqrtf((float)D);
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 o[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](KV16<D>& r, int i) {
+    const int key0 = 16 * i;  // within the wave's range
+    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) sc = mfma16_chunk(sc, r.k[s], qf[s]);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float sv = key0 + 4 * g4 + e < nkeys ? sc[e] * scale : -INFINITY;
+      sc[e] = sv;
+      mx = fmaxf(mx, sv);
+    }
+    mx = fmaxf(mx, shfl_xor(mx, 16));
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - m_new);
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - m_new);
+    l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+    m_run = m_new;
+    if (key0 + 16 > nkeys) {  // keys past the end may hold stale data: zero their values
+      const int nvalid = nkeys - (key0 + 4 * g4);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) r.v[db] = keep_first(r.v[db], nvalid);
+    }
+    const bf16x4 pb = {from_f32<bf16>(p[0]), from_f32<bf16>(p[1]), from_f32<bf16>(p[2]), from_f32<bf16>(p[3])};
+    const u32x2 pw = __builtin_bit_cast(u32x2, pb);
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[db] = mfma16x16x16(o[db] * alpha, r.v[db], pw);
+  };
+
+  // Two register buffers; every iteration issues the same loads (blocks past
+  // the range are empty), so the waits for block i never cover block i+1.
+  if (nblk > 0) {
+    KV16<D> ra, rb;
+    load_kv16<D>(ra, kpool, vpool, btab[0], true, G, g, c16, g4);
+    int id_b = btab[min(1, nblk - 1)];
+#pragma unroll 1
+    for (int i = 0; i < nblk; i += 2) {
+      load_kv16<D>(rb, kpool, vpool, id_b, i + 1 < nblk, G, g, c16, g4);
+      const int id_a = btab[min(i + 2, nblk - 1)];
+      compute(ra, i);
+      load_kv16<D>(ra, kpool, vpool, id_a, i + 2 < nblk, G, g, c16, g4);
+      id_b = btab[min(i + 3, nblk - 1)];
+      if (i + 1 < nblk) compute(rb, i + 1);
+    }
+  }
+
+  // ---- merge the four waves (a wave without keys has m = -inf, l = 0, o = 0) ----
+  l_run += shfl_xor(l_run, 16);
+  l_run += shfl_xor(l_run, 32);
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm[wave][c16][2 + 16 * db + 4 * g4 + e] = o[db][e];
+  if (g4 == 0) {
+    sm[wave][c16][0] = m_run;
+    sm[wave][c16][1] = l_run;
+  }
+  __syncthreads();
+  const int hh = tid >> 4, sub = tid & 15;
+  if (hh >= R) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][hh][0]);
+  float f[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) f[w] = fast_exp2(sm[w][hh][0] - M);  // waves without keys: exp2(-inf) = 0
+  float* dst = part + (((size_t)b * H + g * R + hh) * max_splits + split) * (D + 2);
+  for (int x = sub; x < D + 2; x += 16) {
+    float v;
+    if (x == 0) {
+      v = M;
+    } else {
+      v = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) v += f[w] * sm[w][hh][x];
+    }
+    dst[x] = v;
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* __restrict__ part, T* __restrict__ attn,
                                                                   int max_splits, int H, BatchView batch) {
@@ -267,8 +432,14 @@ hipError_t launch_attn_decode(DType t, const void* q, float* partial, int max_sp
                               const BatchView& b, hipStream_t s) {
   if (H % c.G != 0 || H / c.G > 16) return hipErrorInvalidValue;
   if (t == DType::BF16) {
-    if (c.D == 128) return launch_split<bf16, 128>(q, partial, max_splits, H, c, b, s);
-    if (c.D == 64) return launch_split<bf16, 64>(q, partial, max_splits, H, c, b, s);
+    dim3 grid(c.G * b.batch, max_splits);
+    if (c.D == 128)
+      attn_decode_wave_kernel<128><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(q), partial, max_splits, H, c, b);
+    else if (c.D == 64)
+      attn_decode_wave_kernel<64><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(q), partial, max_splits, H, c, b);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
   } else {
     if (c.D == 64) return launch_split<float, 64>(q, partial, max_splits, H, c, b, s);
   }

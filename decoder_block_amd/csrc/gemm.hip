@@ -27,6 +27,7 @@
 // own L2).
 #include "common.h"
 #include "kernels.h"
+#include <algorithm>
 #include <type_traits>
 
 namespace llk {
@@ -459,6 +460,268 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Skinny bf16 GEMM for few tokens (decode): the weights are streamed once from
+// HBM and the work is bound by that stream, so the shape is chosen for memory
+// parallelism, not reuse.  A workgroup owns 64 features x 64 tokens and one
+// of KS slices of K; each of its four waves walks a quarter of the slice on
+// its own (no barriers in the main loop), loading W and X fragments straight
+// into registers through buffer descriptors (X rows past M read as zeros),
+// three k-steps ahead of the MFMAs.  The four waves add their tiles through
+// LDS; with KS = 1 the epilogue runs directly, otherwise the fp32 partial
+// goes to [ks][M][N] and a second pass adds the KS partials in a fixed order
+// and runs the epilogue.
+// ---------------------------------------------------------------------------
+constexpr int kSkinnyTargetGroups = 512;
+
+// K % 64 == 0: the LDS-staged streaming kernel, one workgroup per CU.  K is
+// split into the largest power of two of slices that keeps the workgroups
+// within one round of the 256 CUs (each further round pays the pipeline
+// ramp-up again), and at least two stages per slice.
+bool skinny_streams(int K) { return K % 64 == 0; }
+
+int skinny_ks(int M, int N, int K) {
+  const int groups = (N / 64) * ((M + 63) / 64);
+  if (skinny_streams(K)) {
+    int ks = 1;
+    while (ks < 16 && groups * ks * 2 <= 256 && K / (128 * ks * 2) >= 1) ks *= 2;
+    return ks;
+  }
+  int ks = (kSkinnyTargetGroups + groups - 1) / groups;
+  ks = std::min(ks, 8);
+  ks = std::min(ks, std::max(1, K / 128));  // every wave keeps at least one 32-deep k-step
+  return std::max(ks, 1);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_skinny_kernel(GemmArgs a, int KS) {
+  constexpr int RS = 68;  // LDS row stride (floats) of the reduction tile
+  __shared__ float red[4][64 * RS];
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64, ks = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
+
+  const int nk = a.K / 32;
+  const int g_beg = nk * ks / KS, g_end = nk * (ks + 1) / KS;
+  const int w_beg = g_beg + (g_end - g_beg) * wave / 4, w_end = g_beg + (g_end - g_beg) * (wave + 1) / 4;
+
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const bf16*>(a.W) + (size_t)n0 * a.K)), 0,
+      64 * a.K * 2, 0x00020000);
+  const int x_rows = min(64, a.M - m0);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const bf16*>(a.X) + (size_t)m0 * a.ldx)), 0,
+      x_rows * a.ldx * 2, 0x00020000);
+  int vw[4], vx[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    vw[i] = ((16 * i + c16) * a.K + 8 * g4) * 2;
+    vx[i] = ((16 * i + c16) * a.ldx + 8 * g4) * 2;
+  }
+  struct Frag {
+    bf16x8 w[4], x[4];
+  };
+  // k-steps past the wave's range move their (range-checked) VGPR offset past
+  // num_records (< 2^30 by the launch check), so they read zeros without traffic
+  auto load = [&](Frag& f, int kt) {
+    const int ko = kt < w_end ? kt * 64 : (1 << 30);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.w[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, vw[i] + ko, 0, 0));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      f.x[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, vx[j] + ko, 0, 0));
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16_chunk(acc[i][j], f.w[i], f.x[j]);
+  };
+  if (w_beg < w_end) {
+    Frag f0, f1, f2;
+    load(f0, w_beg);
+    load(f1, w_beg + 1);
+#pragma unroll 1
+    for (int kt = w_beg; kt < w_end; kt += 3) {
+      load(f2, kt + 2);
+      mma(f0);
+      load(f0, kt + 3);
+      if (kt + 1 < w_end) mma(f1);
+      load(f1, kt + 4);
+      if (kt + 2 < w_end) mma(f2);
+    }
+  }
+
+  // add the four waves' tiles: red[w][feature][token]
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave][(16 * i + 4 * g4 + e) * RS + 16 * j + c16] = acc[i][j][e];
+  __syncthreads();
+  const int tt = tid & 63, fg = tid >> 6;  // token, group of 16 features
+  const int t = m0 + tt;
+  if (t >= a.M) return;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = (16 * fg + 4 * u + e) * RS + tt;
+      v[e] = (red[0][r] + red[1][r]) + (red[2][r] + red[3][r]);
+    }
+    const int f = n0 + 16 * fg + 4 * u;
+    if (KS == 1) {
+      epilogue<bf16, EPI>(a, t, f, v);
+    } else {
+      *reinterpret_cast<f32x4*>(a.split_ws + ((size_t)ks * a.M + t) * a.N + f) = v;
+    }
+  }
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int KS) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // f32x4 index in [M][N / 4]
+  const int n4 = a.N / 4;
+  if (i >= (size_t)a.M * n4) return;
+  const int t = (int)(i / n4), f = (int)(i % n4) * 4;
+  const f32x4* p = reinterpret_cast<const f32x4*>(a.split_ws) + (size_t)t * n4 + f / 4;
+  f32x4 v = p[0];
+  for (int k = 1; k < KS; ++k) v += p[(size_t)k * a.M * n4];
+  epilogue<bf16, EPI>(a, t, f, v);
+}
+
+// ---------------------------------------------------------------------------
+// Weight-streaming bf16 GEMM for few tokens, staged through LDS.  A workgroup
+// owns 64 features x 64 tokens and one of KS slices of K.  Stages of 64
+// K-elements (W: 64 rows x 128 B, X: 64 rows x 128 B) are moved by LDS DMA
+// into a ring of NSL slots, NSL - 1 stages ahead, each DMA instruction
+// fetching whole 128-byte row segments.  Wave w computes features 16w..16w+15
+// for all 64 tokens, so no cross-wave reduction is needed.
+// ---------------------------------------------------------------------------
+struct StreamCfg {
+  static constexpr int NSL = 8;                 // ring slots
+  static constexpr int CPR = 8;                 // 16-byte chunks per row per stage (64 bf16)
+  static constexpr int ROWS = 128;              // 64 W rows, then 64 X rows
+  static constexpr int SLOT = ROWS * CPR;       // chunks per slot (16 KB)
+  static constexpr int PER = SLOT / 256;        // DMAs per thread per stage
+  // chunk position of logical chunk c in row r: XOR with the row spreads a
+  // quarter-wave's 16 rows over all 16-byte bank groups
+  static DEVI int swz(int r, int c) { return r * CPR + (c ^ (r & 7)); }
+};
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a, int KS) {
+  using C = StreamCfg;
+  __shared__ u32x4 ring[C::NSL * C::SLOT];
+  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64, ks = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
+
+  const int nk = a.K / 64;
+  const int s_beg = nk * ks / KS, s_end = nk * (ks + 1) / KS;
+  const int ns = s_end - s_beg;
+
+  // DMA i of this thread: chunk slot (wave * PER + i) * 64 + lane of a stage
+  const char* Wt = reinterpret_cast<const char*>(a.W) + ((size_t)n0 * a.K + (size_t)s_beg * 64) * 2;
+  const char* Xt = reinterpret_cast<const char*>(a.X) + ((size_t)m0 * a.ldx + (size_t)s_beg * 64) * 2;
+  const int x_rows = min(64, a.M - m0);
+  // DMA group q = wave * PER + i covers rows 8q .. 8q + 7: W rows for q < 8,
+  // X rows after (wave-uniform, so the descriptor choice stays scalar)
+  int voff[C::PER];
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) {
+    const int slot = (wave * C::PER + i) * 64 + lane;
+    const int row = slot / C::CPR, c = (slot % C::CPR) ^ (row & 7);
+    voff[i] = row >= 64 ? ((row - 64) * a.ldx + 8 * c) * 2 : (row * a.K + 8 * c) * 2;
+  }
+  const uint32_t ring_base = lds_address(ring);
+  auto issue = [&](int st) {
+    const bool live = st < ns;
+    const int kb = live ? st * 128 : 0;
+    const i32x4 rW = make_rsrc(Wt + kb, live ? (uint32_t)(64 * a.K * 2) : 0u);
+    const i32x4 rX = make_rsrc(Xt + kb, live ? (uint32_t)(x_rows * a.ldx * 2) : 0u);
+    const uint32_t slot_base = ring_base + (uint32_t)((st % C::NSL) * C::SLOT * 16);
+#pragma unroll
+    for (int i = 0; i < C::PER; ++i)
+      buf_dma16_to(wave * C::PER + i >= 8 ? rX : rW, slot_base + (uint32_t)((wave * C::PER + i) * 1024), voff[i]);
+  };
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int st = 0; st < C::NSL - 1; ++st) issue(st);
+#pragma unroll 1
+  for (int st = 0; st < ns; ++st) {
+    wait_vmcnt<(C::NSL - 2) * C::PER>();  // stage st landed (later stages may still be in flight)
+    lds_barrier();                         // ... for every wave; and every wave is done with st - 1
+    issue(st + C::NSL - 1);
+    const u32x4* L = ring + (st % C::NSL) * C::SLOT;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int c = 4 * kk + g4;
+      const bf16x8 fa = __builtin_bit_cast(bf16x8, L[C::swz(16 * wave + c16, c)]);
+      bf16x8 fb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fb[j] = __builtin_bit_cast(bf16x8, L[C::swz(64 + 16 * j + c16, c)]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = mfma16_chunk(acc[j], fa, fb[j]);
+    }
+  }
+  wait_vmcnt<0>();  // the empty DMAs issued past the end have retired
+
+  const int f = n0 + 16 * wave + 4 * g4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = m0 + 16 * j + c16;
+    if (t >= a.M) continue;
+    if (KS == 1)
+      epilogue<bf16, EPI>(a, t, f, acc[j]);
+    else
+      *reinterpret_cast<f32x4*>(a.split_ws + ((size_t)ks * a.M + t) * a.N + f) = acc[j];
+  }
+}
+
+template <int EPI>
+hipError_t launch_skinny_epi(const GemmArgs& a, int KS, hipStream_t s) {
+  dim3 grid(a.N / 64, (a.M + 63) / 64, KS);
+  if (skinny_streams(a.K))
+    gemm_stream_kernel<EPI><<<grid, 256, 0, s>>>(a, KS);
+  else
+    gemm_skinny_kernel<EPI><<<grid, 256, 0, s>>>(a, KS);
+  if (KS > 1) {
+    const size_t n = (size_t)a.M * (a.N / 4);
+    gemm_split_reduce_kernel<EPI><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, KS);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+  if (a.N % 64 != 0 || a.K % 32 != 0 || a.M <= 0) return hipErrorInvalidValue;
+  if ((int64_t)64 * a.K * 2 >= (1ll << 30) || (int64_t)64 * a.ldx * 2 >= (1ll << 30)) return hipErrorInvalidValue;
+  const int KS = skinny_ks(a.M, a.N, a.K);
+  if (KS > 1 && (a.split_ws == nullptr || a.split_ws_bytes < (size_t)KS * a.M * a.N * sizeof(float)))
+    return hipErrorInvalidValue;
+  switch (a.epi) {
+    case Epi::QKV: return launch_skinny_epi<0>(a, KS, s);
+    case Epi::RESID_H: return launch_skinny_epi<1>(a, KS, s);
+    case Epi::SWIGLU: return launch_skinny_epi<2>(a, KS, s);
+    case Epi::RESID_OUT: return launch_skinny_epi<3>(a, KS, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename T, typename C>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   if (a.N % C::BN != 0 || a.K % (2 * C::BK) != 0 || a.M <= 0) return hipErrorInvalidValue;
@@ -498,9 +761,18 @@ using SmallF = Cfg<float, 64, 64, 2, 2>;
 
 int gemm_tile_n(GemmTile t) { return t == GemmTile::LARGE ? 256 : 64; }
 
+int skinny_ksplit(int M, int N, int K) { return skinny_ks(M, N, K); }
+size_t skinny_partial_bytes(int M, int N, int K) {
+  const int ks = skinny_ks(M, N, K);
+  return ks > 1 ? (size_t)ks * M * N * sizeof(float) : 0;
+}
+
 hipError_t launch_gemm(DType t, GemmTile tile, const GemmArgs& a, hipStream_t s) {
-  if (t == DType::BF16)
+  if (t == DType::BF16) {
+    if (tile == GemmTile::SKINNY) return launch_skinny(a, s);
     return tile == GemmTile::LARGE ? launch_big(a, s) : launch_cfg<bf16, SmallBF>(a, s);
+  }
+  if (tile == GemmTile::SKINNY) return hipErrorInvalidValue;
   return tile == GemmTile::LARGE ? launch_cfg<float, LargeF>(a, s) : launch_cfg<float, SmallF>(a, s);
 }
 

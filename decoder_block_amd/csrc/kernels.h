@@ -50,11 +50,20 @@ struct GemmArgs {
   void* out;          // RESID_H: h fp32; SWIGLU: s [M][ldo]; RESID_OUT: out
   int ldo;
   DType out_dtype;    // RESID_OUT only
+  // SKINNY tiles split K over workgroups; their fp32 partial sums [ks][M][N]
+  // go here (skinny_partial_bytes) before one pass adds them and runs the epilogue
+  float* split_ws;
+  size_t split_ws_bytes;
 };
 
-// Tile shape chosen by the host for a GEMM.
-enum class GemmTile : int { LARGE = 0, SMALL = 1 };
+// Tile shape chosen by the host for a GEMM.  SKINNY (bf16, M <= 128) is the
+// weight-streaming shape of decode: 64 x 64 tiles with K split across
+// workgroups so that even N = hidden size fills the chip.
+enum class GemmTile : int { LARGE = 0, SMALL = 1, SKINNY = 2 };
 int gemm_tile_n(GemmTile t);  // features per workgroup tile
+// workgroups a SKINNY GEMM splits K into, and the partial-sum bytes it needs
+int skinny_ksplit(int M, int N, int K);
+size_t skinny_partial_bytes(int M, int N, int K);
 
 hipError_t launch_gemm(DType t, GemmTile tile, const GemmArgs& a, hipStream_t s);
 

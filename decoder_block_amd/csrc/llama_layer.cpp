@@ -107,8 +107,24 @@ PackedLayout packed_layout(const Shape& s) {
 int max_splits_for(const Shape& s) { return (s.max_pos + llk::decode_split_keys() - 1) / llk::decode_split_keys(); }
 
 struct WsLayout {
-  size_t desc, r1, r2, q, attn, h, hb, s, part, total;
+  size_t desc, r1, r2, q, attn, h, hb, s, part, gpart, gpart_bytes, total;
 };
+
+bool use_skinny(const Shape& sh, long M) { return sh.dt == DType::BF16 && M <= 128; }
+
+// Split-K partial sums of the skinny GEMMs, for every token count up to T (the
+// size is non-decreasing in T, so a workspace sized for T serves every call
+// with fewer tokens).
+size_t skinny_ws_bytes(const Shape& sh, size_t T) {
+  if (sh.dt != DType::BF16) return 0;
+  const int shapes[4][2] = {{sh.NQKV_pad, sh.d}, {sh.d, sh.HD}, {2 * sh.I_pad, sh.d}, {sh.d, sh.I_pad}};
+  size_t best = 0;
+  for (const int m : {64, 128}) {
+    const int M = (int)std::min<size_t>(T, (size_t)m);
+    for (const auto& nk : shapes) best = std::max(best, llk::skinny_partial_bytes(M, nk[0], nk[1]));
+  }
+  return best;
+}
 
 WsLayout ws_layout(const Shape& sh, size_t T, size_t B) {
   WsLayout w;
@@ -131,6 +147,9 @@ WsLayout ws_layout(const Shape& sh, size_t T, size_t B) {
   off = align256(off + T * sh.I_pad * sh.es);
   w.part = off;
   off = align256(off + B * sh.H * (size_t)max_splits_for(sh) * (sh.D + 2) * sizeof(float));
+  w.gpart = off;
+  w.gpart_bytes = skinny_ws_bytes(sh, T);
+  off = align256(off + w.gpart_bytes);
   w.total = off;
   return w;
 }
@@ -642,7 +661,9 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
 
   llk::BatchView bv{desc, batch, seq_len};
   llk::CacheView cv = cache_view(c);
+  float* gpart = reinterpret_cast<float*>(W + wl.gpart);
   auto tile_for = [&](int N) {
+    if (use_skinny(s, M)) return llk::GemmTile::SKINNY;
     return (M >= 256 && N % llk::gemm_tile_n(llk::GemmTile::LARGE) == 0) ? llk::GemmTile::LARGE
                                                                           : llk::GemmTile::SMALL;
   };
@@ -655,6 +676,8 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
 
   // QKV + RoPE + cache append
   llk::GemmArgs a{};
+  a.split_ws = gpart;
+  a.split_ws_bytes = wl.gpart_bytes;
   a.W = P + L->pl.qkv;
   a.X = x;
   a.M = M;
@@ -683,6 +706,8 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
 
   // o_proj + residual -> h (fp32)
   llk::GemmArgs o{};
+  o.split_ws = gpart;
+  o.split_ws_bytes = wl.gpart_bytes;
   o.W = P + L->pl.o;
   o.X = attn;
   o.M = M;
@@ -701,6 +726,8 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
 
   // gate/up + SiLU * up
   llk::GemmArgs g{};
+  g.split_ws = gpart;
+  g.split_ws_bytes = wl.gpart_bytes;
   g.W = P + L->pl.gu;
   g.X = hb;
   g.M = M;
@@ -715,6 +742,8 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
 
   // down + residual -> out
   llk::GemmArgs dn{};
+  dn.split_ws = gpart;
+  dn.split_ws_bytes = wl.gpart_bytes;
   dn.W = P + L->pl.down;
   dn.X = sb;
   dn.M = M;

@@ -29,8 +29,15 @@ static std::vector<PackCall> g_packs;
 
 namespace llk {
 int gemm_tile_n(GemmTile t) { return t == GemmTile::LARGE ? 256 : 64; }
+int skinny_ksplit(int, int N, int) { return N <= 8192 ? 4 : 1; }
+size_t skinny_partial_bytes(int M, int N, int K) {
+  const int ks = skinny_ksplit(M, N, K);
+  return ks > 1 ? (size_t)ks * M * N * sizeof(float) : 0;
+}
 hipError_t launch_gemm(DType, GemmTile t, const GemmArgs& a, hipStream_t) {
-  g_log.push_back("gemm" + std::to_string((int)a.epi) + (t == GemmTile::LARGE ? "L" : "S"));
+  const char* tag = t == GemmTile::LARGE ? "L" : (t == GemmTile::SKINNY ? "K" : "S");
+  g_log.push_back("gemm" + std::to_string((int)a.epi) + tag);
+  if (t == GemmTile::SKINNY && a.split_ws_bytes < skinny_partial_bytes(a.M, a.N, a.K)) g_log.push_back("gemm-ws-short");
   return hipSuccess;
 }
 hipError_t launch_rms_rowscale(DType, const void*, float*, int, int, float, hipStream_t) {
@@ -313,6 +320,59 @@ int main() {
   CHECK(llama_kv_cache_free_seq(C, s0) == LLAMA_OK);
   CHECK(llama_kv_cache_destroy(C) == LLAMA_OK);
   CHECK(llama_layer_destroy(L) == LLAMA_OK);
+
+  // bf16 layer: few tokens take the split-K skinny GEMMs, whose partial sums
+  // fit a workspace sized for any larger token count
+  {
+    llama_layer_config cb = tiny();
+    cb.dtype = LLAMA_DTYPE_BF16;
+    cb.max_position = 512;
+    size_t pb = 0;
+    CHECK(llama_layer_packed_bytes(&cb, &pb) == LLAMA_OK);
+    void* packed_b = aligned_buf(pb);
+    llama_layer* Lb = nullptr;
+    CHECK(llama_layer_create(&cb, &w, packed_b, nullptr, &Lb) == LLAMA_OK);
+    size_t w1 = 0, w64 = 0, w100 = 0, w128 = 0, w1000 = 0;
+    CHECK(llama_layer_workspace_bytes(Lb, 1, 1, &w1) == LLAMA_OK);
+    CHECK(llama_layer_workspace_bytes(Lb, 64, 1, &w64) == LLAMA_OK);
+    CHECK(llama_layer_workspace_bytes(Lb, 100, 1, &w100) == LLAMA_OK);
+    CHECK(llama_layer_workspace_bytes(Lb, 128, 1, &w128) == LLAMA_OK);
+    CHECK(llama_layer_workspace_bytes(Lb, 1000, 1, &w1000) == LLAMA_OK);
+    CHECK(w1 <= w64 && w64 <= w100 && w100 <= w128 && w128 <= w1000);
+    size_t cbytes = 0;
+    CHECK(llama_kv_cache_bytes(&cb, 40, 16, 2, &cbytes) == LLAMA_OK);
+    void* pool_b = aligned_buf(cbytes);
+    llama_kv_cache* Cb = nullptr;
+    CHECK(llama_kv_cache_create(&cb, 40, 16, 2, nullptr, pool_b, &Cb) == LLAMA_OK);
+    int32_t sa = -1, sb = -1;
+    CHECK(llama_kv_cache_add_seq(Cb, &sa) == LLAMA_OK && llama_kv_cache_add_seq(Cb, &sb) == LLAMA_OK);
+    void* wsb2 = aligned_buf(w1000);
+    void* xb = aligned_buf(2 * 300 * 256 * 2);
+    void* ob = aligned_buf(2 * 300 * 256 * 4);
+    int32_t ids2[2] = {sa, sb};
+    g_log.clear();
+    CHECK(llama_layer_prefill(Lb, Cb, 2, 50, ids2, xb, ob, LLAMA_DTYPE_F32, wsb2, nullptr) == LLAMA_OK);
+    {
+      const std::vector<std::string> want = {"rms1", "gemm0K", "attn_prefill", "gemm1K", "rms2", "gemm2K", "gemm3K"};
+      CHECK(g_log == want);
+    }
+    g_log.clear();
+    CHECK(llama_layer_decode(Lb, Cb, 2, ids2, xb, ob, LLAMA_DTYPE_BF16, wsb2, nullptr) == LLAMA_OK);
+    CHECK(g_log.size() == 8 && g_log[1] == "gemm0K" && g_log[7] == "gemm3K");
+    g_log.clear();
+    CHECK(llama_layer_prefill(Lb, Cb, 1, 300, ids2, xb, ob, LLAMA_DTYPE_F32, wsb2, nullptr) == LLAMA_OK);
+    {
+      const std::vector<std::string> want = {"rms1", "gemm0L", "attn_prefill", "gemm1L", "rms2", "gemm2L", "gemm3L"};
+      CHECK(g_log == want);
+    }
+    CHECK(llama_kv_cache_destroy(Cb) == LLAMA_OK);
+    CHECK(llama_layer_destroy(Lb) == LLAMA_OK);
+    std::free(pool_b);
+    std::free(wsb2);
+    std::free(xb);
+    std::free(ob);
+    std::free(packed_b);
+  }
   std::free(pool);
   std::free(ws);
   std::free(x);
