@@ -68,7 +68,10 @@ size_t skinny_partial_bytes(int M, int N, int K);
 hipError_t launch_gemm(DType t, GemmTile tile, const GemmArgs& a, hipStream_t s);
 
 // RMSNorm row scale r[t] = rsqrt(mean(x[t]^2) + eps) of x [M][d] (layer dtype).
-hipError_t launch_rms_rowscale(DType t, const void* x, float* r, int M, int d, float eps,
+struct Upload;
+// `up` (may be null) is a batch of int32 stores applied by the same launch
+// before any later kernel on the stream runs (host bookkeeping of the step).
+hipError_t launch_rms_rowscale(DType t, const void* x, float* r, int M, int d, float eps, const Upload* up,
                                hipStream_t s);
 // Second norm: r2[t] from h [M][d] fp32, plus hb = h * gamma (fp32 gamma) rounded
 // once to the layer dtype.
@@ -100,7 +103,7 @@ hipError_t launch_to_f32(DType t, const void* src, float* dst, int n, hipStream_
 // Small host -> device updates carried in kernel arguments: base[idx[i]] = val[i].
 constexpr int kUploadMax = 240;
 struct Upload {
-  int32_t* base;
+  int32_t* base[2];  // entry i stores val[i] at base[idx[i] >> 31][idx[i] & 0x7fffffff]
   int n;
   int32_t idx[kUploadMax];
   int32_t val[kUploadMax];

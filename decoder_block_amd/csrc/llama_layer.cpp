@@ -292,18 +292,39 @@ llk::CacheView cache_view(const llama_kv_cache* c) {
 }
 
 // Flush (index, value) pairs to device int32 memory through kernel arguments.
+// Host-side int32 stores for the device (block tables, batch descriptors),
+// batched into kernel arguments: a batch holds up to kUploadMax stores to at
+// most two arrays.
 struct Uploader {
   std::vector<llk::Upload> batches;
   void add(int32_t* base, int32_t idx, int32_t val) {
-    if (batches.empty() || batches.back().base != base || batches.back().n == llk::kUploadMax) {
+    int slot = -1;
+    if (!batches.empty() && batches.back().n < llk::kUploadMax) {
+      llk::Upload& u = batches.back();
+      if (u.base[0] == base) slot = 0;
+      else if (u.base[1] == base || u.base[1] == nullptr) slot = 1;
+    }
+    if (slot < 0) {
       batches.emplace_back();
       std::memset(&batches.back(), 0, sizeof(llk::Upload));
-      batches.back().base = base;
+      slot = 0;
     }
     llk::Upload& u = batches.back();
-    u.idx[u.n] = idx;
+    u.base[slot] = base;
+    u.idx[u.n] = idx | (slot ? (int32_t)0x80000000u : 0);
     u.val[u.n] = val;
     ++u.n;
+  }
+  // launch every batch but the last, which is returned for the caller's first
+  // kernel to apply (null if there is none)
+  hipError_t flush_all_but_last(hipStream_t s, const llk::Upload** last) {
+    *last = nullptr;
+    for (size_t i = 0; i + 1 < batches.size(); ++i) {
+      hipError_t e = llk::launch_upload(batches[i], s);
+      if (e != hipSuccess) return e;
+    }
+    if (!batches.empty()) *last = &batches.back();
+    return hipSuccess;
   }
   hipError_t flush(hipStream_t s) {
     for (auto& u : batches) {
@@ -645,7 +666,9 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
   }
   // lengths are committed now: every later failure is a device failure
   for (int b = 0; b < batch; ++b) c->seqs[seq_ids[b]].len += seq_len;
-  HIP_TRY(up.flush(hs));
+  // the last upload batch rides on the first norm kernel's launch
+  const llk::Upload* last_upload = nullptr;
+  HIP_TRY(up.flush_all_but_last(hs, &last_upload));
 
   float* r1 = reinterpret_cast<float*>(W + wl.r1);
   float* r2 = reinterpret_cast<float*>(W + wl.r2);
@@ -672,7 +695,7 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
                  batch, seq_len, M, s.d, s.H, s.G, s.D, s.I);
 
   // RMSNorm_1 statistics
-  HIP_TRY(timed(L, K_RMS1, hs, [&] { return llk::launch_rms_rowscale(s.dt, x, r1, M, s.d, eps, hs); }));
+  HIP_TRY(timed(L, K_RMS1, hs, [&] { return llk::launch_rms_rowscale(s.dt, x, r1, M, s.d, eps, last_upload, hs); }));
 
   // QKV + RoPE + cache append
   llk::GemmArgs a{};

@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void to_f32_kernel(const T* __restrict__ src, 
 }
 
 __global__ __launch_bounds__(256) void upload_kernel(Upload u) {
-  for (int i = threadIdx.x; i < u.n; i += 256) u.base[u.idx[i]] = u.val[i];
+  for (int i = threadIdx.x; i < u.n; i += 256) u.base[(u.idx[i] >> 31) & 1][u.idx[i] & 0x7fffffff] = u.val[i];
 }
 
 // K pool [blk][G][16][D]; V pool [blk][G][D][16] (V transposed per block).

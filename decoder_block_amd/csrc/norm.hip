@@ -5,7 +5,8 @@
 // components, one by one", 3.2.1).  gamma is folded into the weights of the
 // projection that follows, and the row scale r is applied in that GEMM's
 // epilogue, so the norm itself is one HBM pass that writes 4 bytes per row.
-// One wavefront per row, 16-byte loads, shuffle reduction.
+// One wavefront per row, 16-byte loads (eight in flight per lane), shuffle
+// reduction.
 #include "common.h"
 #include "kernels.h"
 
@@ -20,12 +21,15 @@ DEVI float wave_sum(float v) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void rms_rowscale_kernel(const T* __restrict__ x, float* __restrict__ r,
-                                                           int M, int d, float eps) {
+                                                           int M, int d, float eps, Upload u) {
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < u.n; i += 256) u.base[(u.idx[i] >> 31) & 1][u.idx[i] & 0x7fffffff] = u.val[i];
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
   const T* p = x + (size_t)row * d;
   float acc = 0.f;
+#pragma unroll 8
   for (int c = lane * Chunk<T>::N; c < d; c += 64 * Chunk<T>::N) {
     auto v = load_chunk<T>(p + c);
 #pragma unroll
@@ -51,6 +55,7 @@ __global__ __launch_bounds__(256) void rms_convert_kernel(const float* __restric
   const float* p = h + (size_t)row * d;
   T* q = hb + (size_t)row * d;
   float acc = 0.f;
+#pragma unroll 8
   for (int c = lane * 4; c < d; c += 64 * 4) {
     f32x4 v = *reinterpret_cast<const f32x4*>(p + c);
     acc += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
@@ -68,12 +73,20 @@ __global__ __launch_bounds__(256) void rms_convert_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_rms_rowscale(DType t, const void* x, float* r, int M, int d, float eps, hipStream_t s) {
+hipError_t launch_rms_rowscale(DType t, const void* x, float* r, int M, int d, float eps, const Upload* up,
+                               hipStream_t s) {
   const int grid = (M + 3) / 4;
+  Upload u;
+  if (up) {
+    u = *up;
+  } else {
+    u.base[0] = u.base[1] = nullptr;
+    u.n = 0;
+  }
   if (t == DType::BF16)
-    rms_rowscale_kernel<bf16><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(x), r, M, d, eps);
+    rms_rowscale_kernel<bf16><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(x), r, M, d, eps, u);
   else
-    rms_rowscale_kernel<float><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(x), r, M, d, eps);
+    rms_rowscale_kernel<float><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(x), r, M, d, eps, u);
   return hipGetLastError();
 }
 

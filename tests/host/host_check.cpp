@@ -24,6 +24,7 @@ static int g_fail = 0;
 
 static std::vector<std::string> g_log;
 static int g_events = 0;
+static int g_uploads = 0;
 struct PackCall { int rows, cols, ldd, row_mul, row_add; bool gamma; };
 static std::vector<PackCall> g_packs;
 
@@ -40,8 +41,13 @@ hipError_t launch_gemm(DType, GemmTile t, const GemmArgs& a, hipStream_t) {
   if (t == GemmTile::SKINNY && a.split_ws_bytes < skinny_partial_bytes(a.M, a.N, a.K)) g_log.push_back("gemm-ws-short");
   return hipSuccess;
 }
-hipError_t launch_rms_rowscale(DType, const void*, float*, int, int, float, hipStream_t) {
+hipError_t launch_upload(const Upload& u, hipStream_t);
+hipError_t launch_rms_rowscale(DType, const void*, float*, int, int, float, const Upload* up, hipStream_t s) {
   g_log.push_back("rms1");
+  if (up) {  // the batch riding on this launch is applied like a standalone upload
+    if (launch_upload(*up, s) != hipSuccess) return hipErrorUnknown;
+    --g_uploads;  // not a launch of its own
+  }
   return hipSuccess;
 }
 hipError_t launch_rms_convert(DType, const float*, const float*, void*, float*, int, int, float, hipStream_t) {
@@ -90,7 +96,8 @@ hipError_t launch_zero(void* dst, size_t bytes, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_upload(const Upload& u, hipStream_t) {
-  for (int i = 0; i < u.n; ++i) u.base[u.idx[i]] = u.val[i];
+  for (int i = 0; i < u.n; ++i) u.base[(u.idx[i] >> 31) & 1][u.idx[i] & 0x7fffffff] = u.val[i];
+  ++g_uploads;
   return hipSuccess;
 }
 hipError_t copy_to_device(void* dst, const void* src, size_t bytes, hipStream_t) {
@@ -357,7 +364,9 @@ int main() {
       CHECK(g_log == want);
     }
     g_log.clear();
+    const int uploads_before = g_uploads;
     CHECK(llama_layer_decode(Lb, Cb, 2, ids2, xb, ob, LLAMA_DTYPE_BF16, wsb2, nullptr) == LLAMA_OK);
+    CHECK(g_uploads == uploads_before);  // block table + descriptors ride on the first norm launch
     CHECK(g_log.size() == 8 && g_log[1] == "gemm0K" && g_log[7] == "gemm3K");
     g_log.clear();
     CHECK(llama_layer_prefill(Lb, Cb, 1, 300, ids2, xb, ob, LLAMA_DTYPE_F32, wsb2, nullptr) == LLAMA_OK);
