@@ -31,6 +31,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_llama3_8b_prefill_decode.md")
+
+
+def traffic_record(kernel: str):
+    """HBM traffic of `kernel` from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel's sources changed since it was taken."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+    except OSError:
+        return None
+    for line in lines:
+        parts = line.split()
+        if not parts or parts[0] != "traffic-record":
+            continue
+        rec = dict(p.split("=", 1) for p in parts[1:])
+        if rec.get("kernel") != kernel:
+            continue
+        h = hashlib.sha256()
+        try:
+            for src in rec["sources"].split(","):
+                h.update(open(os.path.join(ROOT, src), "rb").read())
+        except OSError:
+            return None
+        return rec if h.hexdigest() == rec.get("sha256") else None
+    return None
+
+
 def prefill_flops(w) -> dict:
     """Algorithmic flops per kernel family of one prefill (causal pairs only)."""
     T = w.batch * w.seq_len
@@ -83,12 +111,14 @@ def run_prefill(args, torch, L, synth):
     dom_ms = prof[dom][1] / prof[dom][0]
     ach = flops[dom] / (dom_ms * 1e-3) / 1e12
     total_flops = sum(flops.values())
+    rec = traffic_record(dom)
+    traffic = int(rec["bytes_per_launch"]) if rec and "bytes_per_launch" in rec else None
     log(f"[bench] prefill {ms:.3f} ms/step, layer {total_flops / ms / 1e9:.1f} TFLOP/s")
     res = {
         "tokens_per_s": w.batch * w.seq_len / (ms * 1e-3), "ms": ms, "kernels": kern,
         "layer_tflops": total_flops / (ms * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": flops[dom], "avg_launch_ms": round(dom_ms, 4)},
     }
     layer.close()
@@ -154,6 +184,9 @@ def run_decode(args, torch, L, synth):
     dom = "attn_decode_split"
     dom_ms = prof[dom][1] / prof[dom][0]
     ach = kv_bytes_prof / (dom_ms * 1e-3) / 1e9
+    rec = traffic_record(dom)
+    traffic = (round(float(rec["ratio_to_algorithmic"]) * kv_bytes_prof)
+               if rec and "ratio_to_algorithmic" in rec else None)
     kern = {n: {"avg_us": round(t / c * 1e3, 2), "launches": c} for n, (c, t) in prof.items()}
     step_bytes = kv_bytes + weight_bytes
     log(f"[bench] decode {us:.1f} us/step ({us_prof:.1f} with per-kernel events), "
@@ -164,7 +197,7 @@ def run_decode(args, torch, L, synth):
         "mean_context": float(np.mean(ctx_start)), "kernels": kern,
         "step_hbm_frac": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": kv_bytes_prof, "avg_launch_ms": round(dom_ms, 4)},
     }
     layer.close()
