@@ -121,6 +121,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
     wmax = max(wmax, __shfl_xor(wmax, m, 64));
     wmin = min(wmin, __shfl_xor(wmin, m, 64));
   }
+  // equal in every lane after the butterfly; in SGPRs the tile tests below are
+  // uniform branches instead of per-element selects
+  wmax = __builtin_amdgcn_readfirstlane(wmax);
+  wmin = __builtin_amdgcn_readfirstlane(wmin);
   const int last_s = min(S, (rb + 1) * P) - 1;
   const int ntiles = (start + last_s) / C::KT + 1;
   const u32x4 zero = {0u, 0u, 0u, 0u};
@@ -248,22 +252,25 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
         for (int x = 0; x < C::RB; ++x) sc[x] = mfma32_chunk(sc[x], a, qf[x][kk]);
       }
       // ---- online softmax (lane = one query row per block) ----
-      const bool need_mask = kh + 31 > wmin;
+      // Only the halves that reach the diagonal of some row of this wave need
+      // the causal mask; the test is wave-uniform, so the common case takes
+      // the branch without any per-element compare.
       float mx[C::RB];
       bool grow = false;
+      if (kh + 31 > wmin) {
+#pragma unroll
+        for (int x = 0; x < C::RB; ++x)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kp = kh + 8 * (i >> 2) + 4 * hl + (i & 3);
+            if (kp > qpos[x]) sc[x][i] = -INFINITY;
+          }
+      }
 #pragma unroll
       for (int x = 0; x < C::RB; ++x) {
         float m = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float sv = sc[x][i];
-          if (need_mask) {
-            const int kp = kh + 8 * (i >> 2) + 4 * hl + (i & 3);
-            if (kp > qpos[x]) sv = -INFINITY;
-          }
-          sc[x][i] = sv;
-          m = fmaxf(m, sv);
-        }
+        for (int i = 0; i < 16; ++i) m = fmaxf(m, sc[x][i]);
         mx[x] = fmaxf(m, __shfl_xor(m, 32, 64));
         grow = grow || (mx[x] - m_run[x]) * scale > kRescaleLog2;
       }
