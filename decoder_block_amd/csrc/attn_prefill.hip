@@ -152,23 +152,23 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
     return u == 0 ? blk[0] : u == 1 ? blk[1] : u == 2 ? blk[2] : blk[3];
   };
 
-  // Tile kt -> LDS stage st.  Every 16-byte slot is owned by one lane: it is
-  // either filled by the LDS DMA (global_load_lds_dwordx4: lane i of a wave
-  // lands at base + 16 i) or, for keys past the end, zeroed.
+  // Tile kt -> LDS stage st.  Every 16-byte slot is owned by one lane and
+  // filled by the LDS DMA (global_load_lds_dwordx4: lane i of a wave lands at
+  // base + 16 i).  Keys past the end of the sequence are clamped into its
+  // last block, so every lane loads from an allocated block with no branch:
+  // their scores are masked (every query row precedes them) and `finish`
+  // zeroes their values.
   auto issue = [&](int kt, int st, i32x4v blk) {
+    const int last = kv_len - 1;
 #pragma unroll
     for (int i = 0; i < C::LK; ++i) {
       const int base = (wave * C::LK + i) * 64;
       const int slot = base + lane;
       const int key = slot / C::CPRK;
       const int c = (slot % C::CPRK) ^ k_swz<C::CPRK>(key);
-      const int kp = kt * C::KT + key;
-      if (kp < kv_len) {
-        const size_t bk = (size_t)pick(blk, key >> 4);
-        lds_dma16(kpool + ((bk * G + g) * 16 + (kp & 15)) * D + c * C::CH, &sK[st][base]);
-      } else {
-        sK[st][slot] = zero;
-      }
+      const int kp = min(kt * C::KT + key, last);
+      const size_t bk = (size_t)pick(blk, (kp - kt * C::KT) >> 4);
+      lds_dma16(kpool + ((bk * G + g) * 16 + (kp & 15)) * D + c * C::CH, &sK[st][base]);
     }
 #pragma unroll
     for (int i = 0; i < C::LV; ++i) {
@@ -176,17 +176,14 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
       const int slot = base + lane;
       const int d = slot / C::VROW;
       const int c = (slot % C::VROW) ^ v_swz<C::VROW>(d);
-      const int kp = kt * C::KT + c * C::CH;  // first key of this chunk
-      if (kp < kv_len) {
-        const size_t bk = (size_t)pick(blk, (c * C::CH) >> 4);
-        lds_dma16(vpool + ((bk * G + g) * D + d) * 16 + (kp & 15), &sV[st][base]);
-      } else {
-        sV[st][slot] = zero;
-      }
+      const int kp = min(kt * C::KT + c * C::CH, last & ~(C::CH - 1));  // first key of this chunk
+      const size_t bk = (size_t)pick(blk, (kp - kt * C::KT) >> 4);
+      lds_dma16(vpool + ((bk * G + g) * D + d) * 16 + (kp & 15), &sV[st][base]);
     }
   };
-  // After the DMA has landed: zero values of keys past the end inside a loaded
-  // chunk (they may hold stale data of another sequence).  Only the last tile.
+  // After the DMA has landed: zero the values of keys past the end (a chunk
+  // that reaches past it may hold stale data of another sequence, and the
+  // chunks past it hold a clamped copy).  Only the last tile has any.
   auto finish = [&](int kt, int st) {
     if ((kt + 1) * C::KT <= kv_len) return;
 #pragma unroll
@@ -195,7 +192,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
       const int d = slot / C::VROW;
       const int c = (slot % C::VROW) ^ v_swz<C::VROW>(d);
       const int kp = kt * C::KT + c * C::CH;
-      if (kp < kv_len && kp + C::CH > kv_len) {
+      if (kp + C::CH > kv_len) {
         vec v = __builtin_bit_cast(vec, sV[st][slot]);
 #pragma unroll
         for (int e = 0; e < C::CH; ++e)
@@ -244,13 +241,46 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
 #pragma unroll
         for (int i = 0; i < 16; ++i) sc[x][i] = 0.f;
       const int key = 32 * kb + (lane & 31);
+      // all K fragments of the half are read before the first MFMA, so the
+      // LDS latency is paid once per half, not once per k-step
+      vec ka[C::NQ];
 #pragma unroll
       for (int kk = 0; kk < C::NQ; ++kk) {
         const int c = 2 * kk + hl;
-        const vec a = __builtin_bit_cast(vec, sK[st][key * C::CPRK + (c ^ k_swz<C::CPRK>(key))]);
-#pragma unroll
-        for (int x = 0; x < C::RB; ++x) sc[x] = mfma32_chunk(sc[x], a, qf[x][kk]);
+        ka[kk] = __builtin_bit_cast(vec, sK[st][key * C::CPRK + (c ^ k_swz<C::CPRK>(key))]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < C::NQ; ++kk)
+#pragma unroll
+        for (int x = 0; x < C::RB; ++x) sc[x] = mfma32_chunk(sc[x], ka[kk], qf[x][kk]);
+      // the V^T fragments of the half are read now: their latency hides
+      // behind the softmax below
+      const char* vb = reinterpret_cast<const char*>(&sV[st][0]);
+      vec va[2][C::NDB][8 / C::CH];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        // A operand: lane (row d, group hl) supplies keys 16m+4hl+{0..3} and
+        // 16m+8+4hl+{0..3}, matching the keys its P registers hold.
+        const int kA = 32 * kb + 16 * m + 4 * hl, kB = kA + 8;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          const int d = 32 * db + (lane & 31);
+          auto piece = [&](int kk2) {  // 4 consecutive keys of row d
+            const int byte = kk2 * (int)sizeof(T);
+            return vb + (size_t)(d * C::VROW + ((byte >> 4) ^ v_swz<C::VROW>(d))) * 16 + (byte & 15);
+          };
+          if constexpr (sizeof(T) == 2) {
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(piece(kA));
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(piece(kB));
+            va[m][db][0] = __builtin_bit_cast(vec, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          } else {
+            va[m][db][0] = *reinterpret_cast<const vec*>(piece(kA));
+            va[m][db][8 / C::CH - 1] = *reinterpret_cast<const vec*>(piece(kB));
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
       // ---- online softmax (lane = one query row per block) ----
       // Only the halves that reach the diagonal of some row of this wave need
       // the causal mask; the test is wave-uniform, so the common case takes
@@ -300,36 +330,19 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
       }
 
       // ---- O^T += V^T P^T: each V^T fragment feeds both row blocks ----
-      // A operand: lane (row d, group hl) supplies keys 16m+4hl+{0..3} and
-      // 16m+8+4hl+{0..3}, matching the keys its P registers hold.
-      const char* vb = reinterpret_cast<const char*>(&sV[st][0]);
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const int kA = 32 * kb + 16 * m + 4 * hl, kB = kA + 8;
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          const int d = 32 * db + (lane & 31);
-          auto piece = [&](int kk2) {  // 4 consecutive keys of row d
-            const int byte = kk2 * (int)sizeof(T);
-            return vb + (size_t)(d * C::VROW + ((byte >> 4) ^ v_swz<C::VROW>(d))) * 16 + (byte & 15);
-          };
-          if constexpr (sizeof(T) == 2) {
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(piece(kA));
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(piece(kB));
-            const vec a = __builtin_bit_cast(vec, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
-            for (int x = 0; x < C::RB; ++x) o[x][db] = mfma32_chunk(o[x][db], a, pv[x][m][0]);
-          } else {
-            const vec a0 = *reinterpret_cast<const vec*>(piece(kA));
-            const vec a1 = *reinterpret_cast<const vec*>(piece(kB));
-#pragma unroll
-            for (int x = 0; x < C::RB; ++x) {
-              o[x][db] = mfma32_chunk(o[x][db], a0, pv[x][m][0]);
-              o[x][db] = mfma32_chunk(o[x][db], a1, pv[x][m][8 / C::CH - 1]);
+          for (int x = 0; x < C::RB; ++x) {
+            if constexpr (sizeof(T) == 2) {
+              o[x][db] = mfma32_chunk(o[x][db], va[m][db][0], pv[x][m][0]);
+            } else {
+              o[x][db] = mfma32_chunk(o[x][db], va[m][db][0], pv[x][m][0]);
+              o[x][db] = mfma32_chunk(o[x][db], va[m][db][8 / C::CH - 1], pv[x][m][8 / C::CH - 1]);
             }
           }
-        }
-      }
     }
     if (kt + 1 < ntiles) {
       wait_all_loads();

@@ -111,6 +111,11 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// Workgroup barrier with no wait of its own: for callers that have already
+// ordered the memory the barrier publishes (the memory clobber keeps the
+// compiler from moving memory accesses across it).
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
 // Wait until at most N vector-memory operations of this wave are outstanding
 // (gfx9 s_waitcnt encoding: vmcnt bits [3:0] and [15:14], expcnt and lgkmcnt
 // left at their maxima, i.e. not waited on).

@@ -284,33 +284,41 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
 // Large bf16 tiles: 256 features x 256 tokens, four waves (one per SIMD), each
 // wave 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 whose
 // accumulators (256 registers) stay in the matrix core's register file.
-// A stage is 32 elements of K (two k-steps of 16) held in one slot of a
-// four-slot LDS ring.  Each k-step is 8 slices of two MFMAs plus one LDS read
-// of the next k-step's fragments (read in the order the MFMAs consume them),
-// so with a single wave per SIMD the matrix core does not wait for LDS:
+// A stage is 8 CPR elements of K (CPR / 2 k-steps of 16) held in one slot of
+// an NS-slot LDS ring (in use: CPR 4, NS 4, i.e. 32-element stages in 4
+// slots).  Each k-step is 8 slices of two MFMAs plus one LDS read of the next
+// k-step's fragments (read in the order the MFMAs consume them), so with a
+// single wave per SIMD the matrix core does not wait for LDS:
 //   k-step 0 of stage kt: MFMAs || reads of k-step 1;
-//   wait for this wave's DMAs of stage kt+1, barrier (every wave now holds
-//   all of stage kt in registers);
-//   k-step 1: MFMAs || reads of k-step 0 of stage kt+1 || one DMA per slice
-//   of stage kt+4 into stage kt's slot.
+//   wait for this wave's DMAs of stage kt+1, barrier (every wave is done
+//   with stage kt-1);
+//   last k-step: MFMAs || reads of k-step 0 of stage kt+1 || DMAs of stage
+//   kt+NS-1 into stage kt-1's slot, spread over the slices.
+// Waves 0-1 move the W rows of a stage and waves 2-3 the X rows.
 // 32x32 result layout: lane l holds token (l & 31) and, in registers
 // 4g..4g+3, features 8g + 4(l >> 5) + {0..3}: four lane-local groups of four
 // consecutive features, so the same epilogues apply.
 // ---------------------------------------------------------------------------
+template <int CPR_, int NS_>
 struct BigCfg {
-  static constexpr int BN = 256, BM = 256, NT = 256, CPR = 4, BK = 32, NS = 4;
-  static constexpr int LW = BN * CPR / NT, LX = BM * CPR / NT;  // 16-byte DMAs per thread per stage
-  static constexpr int SLOT = (BN + BM) * CPR;                    // 16-byte chunks per slot
+  static constexpr int BN = 256, BM = 256, NT = 256, CPR = CPR_, NS = NS_, KS = CPR / 2, BK = 8 * CPR;
+  static constexpr int PER = (BN + BM) * CPR / NT;  // DMAs per thread per stage
+  static constexpr int SLOT = (BN + BM) * CPR;      // 16-byte chunks per slot
+  static_assert(CPR == 4 || CPR == 8, "32 or 64 K-elements per stage");
+  static_assert(PER % 8 == 0, "DMAs spread evenly over the 8 slices of a k-step");
+  // 16 consecutive rows read one chunk each: the XOR spreads them over all
+  // 16-byte positions of a 256-byte bank window
+  static DEVI int swz(int r, int c) {
+    if constexpr (CPR == 4) return r * 4 + (c ^ ((r >> 2) & 3));
+    else return r * 8 + (c ^ ((r >> 1) & 7));
+  }
 };
 
-template <int EPI>
+template <int EPI, int CPR, int NS>
 __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
-  using C = BigCfg;
+  using C = BigCfg<CPR, NS>;
   using T = bf16;
-  __shared__ u32x4 L0[C::SLOT];
-  __shared__ u32x4 L1[C::SLOT];
-  __shared__ u32x4 L2[C::SLOT];
-  __shared__ u32x4 L3[C::SLOT];
+  __shared__ u32x4 ring[NS * C::SLOT];
 
   const int tiles_n = a.N / C::BN;
   const int tiles_m = (a.M + C::BM - 1) / C::BM;
@@ -326,33 +334,26 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
   const int tn = (pid % per_group) / gsize;
   const int n0 = tn * C::BN, m0 = tm * C::BM;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
 
-  // DMA i of this lane: W rows for i < LW, X rows after; slot s of a stage
-  // holds logical chunk (s % 4) ^ swizzle(row) of row s / 4
-  constexpr int ES = 2, PER = C::LW + C::LX;
-  int voff[PER];
+  constexpr int ES = 2;
+  int voff[C::PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int slot = ((i < C::LW ? wave * C::LW + i : wave * C::LX + i - C::LW)) * 64 + lane;
-    const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
-    voff[i] = (row * (i < C::LW ? a.K : a.ldx) + c * 8) * ES;
+  for (int i = 0; i < C::PER; ++i) {
+    const int slot = (wave * C::PER + i) * 64 + lane;
+    const int row = slot / C::CPR;
+    const int c = C::swz(row, slot % C::CPR) - row * C::CPR;
+    voff[i] = row < C::BN ? (row * a.K + 8 * c) * ES : ((row - C::BN) * a.ldx + 8 * c) * ES;
   }
-  // LDS byte address (wave-uniform) where DMA i of this wave lands, relative to its slot
-  auto dma_lds = [&](int i) {
-    return (i < C::LW ? (wave * C::LW + i) * 1024 : C::BN * C::CPR * 16 + (wave * C::LX + i - C::LW) * 1024);
-  };
   const char* Wt = reinterpret_cast<const char*>(a.W) + (size_t)n0 * a.K * ES;
   const char* Xt = reinterpret_cast<const char*>(a.X) + (size_t)m0 * a.ldx * ES;
   const uint64_t xb = (uint64_t)(a.M - m0) * (uint64_t)a.ldx * ES;
   const int x_bytes = __builtin_amdgcn_readfirstlane((int)(xb < 0x7fffffffull ? xb : 0x7fffffffull));
   const int nk = a.K / C::BK;
-  const uint32_t base[4] = {lds_address(L0), lds_address(L1), lds_address(L2), lds_address(L3)};
+  const uint32_t ring_base = lds_address(ring);
 
-  // buffer descriptors of stage kt; stages past the end get empty buffers
-  // (no memory moves, but every stage has the same DMA count to wait on)
   auto rsrc_w = [&](int kt) {
     const bool live = kt < nk;
     return make_rsrc(Wt + (live ? kt * C::BK * ES : 0), live ? 0x7fffffffu : 0u);
@@ -363,7 +364,8 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
     return make_rsrc(Xt + kb, live ? (uint32_t)(x_bytes - kb) : 0u);
   };
   auto dma = [&](int i, const i32x4& rW, const i32x4& rX, uint32_t slot_base) {
-    buf_dma16_to(i < C::LW ? rW : rX, slot_base + dma_lds(i), voff[i]);
+    const int q = wave * C::PER + i;  // DMA group: W rows while q * 64 < BN * CPR
+    buf_dma16_to(q * 64 < C::BN * C::CPR ? rW : rX, slot_base + (uint32_t)(q * 1024), voff[i]);
   };
 
   f32x16 acc[4][4];
@@ -375,19 +377,17 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int l32 = lane & 31, lh = lane >> 5;
-  // fragment r of a k-step, in the order the MFMAs first use them:
-  // A0, B0, B1, B2, B3, A1, A2, A3 (MFMAs run (i, j) i-major)
   bf16x8 fr0[8], fr1[8];
+  // fragment r of k-step ks, in the order the MFMAs first use them:
+  // A0, B0, B1, B2, B3, A1, A2, A3 (MFMAs run (i, j) i-major)
   auto frag_addr = [&](int r, int ks) {
     const int c = 2 * ks + lh;
-    if (r == 0) return C::BN * 0 + swz(wn * 128 + l32, c);
-    if (r <= 4) return C::BN * C::CPR + swz(wm * 128 + 32 * (r - 1) + l32, c);
-    return swz(wn * 128 + 32 * (r - 4) + l32, c);
+    if (r == 0) return C::swz(wn * 128 + l32, c);
+    if (r <= 4) return C::swz(C::BN + wm * 128 + 32 * (r - 1) + l32, c);
+    return C::swz(wn * 128 + 32 * (r - 4) + l32, c);
   };
   auto fa = [](bf16x8 (&f)[8], int i) -> bf16x8& { return i == 0 ? f[0] : f[4 + i]; };
   auto fb = [](bf16x8 (&f)[8], int j) -> bf16x8& { return f[1 + j]; };
-  // one k-step: 8 slices of {2 MFMAs from cur, read fragment r of the next
-  // k-step into nxt (from slot L, k-step nks), DMA r if requested}
   auto kstep = [&](bf16x8 (&cur)[8], bf16x8 (&nxt)[8], const u32x4* L, int nks, bool with_dma, const i32x4& rW,
                    const i32x4& rX, uint32_t dma_base) {
 #pragma unroll
@@ -396,54 +396,64 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
       acc[i][j0] = mfma32_chunk(acc[i][j0], fa(cur, i), fb(cur, j0));
       acc[i][j0 + 1] = mfma32_chunk(acc[i][j0 + 1], fa(cur, i), fb(cur, j0 + 1));
       nxt[r] = __builtin_bit_cast(bf16x8, L[frag_addr(r, nks)]);
-      if (with_dma) dma(r, rW, rX, dma_base);
+      if (with_dma) {
+#pragma unroll
+        for (int u = 0; u < C::PER / 8; ++u) dma(r * (C::PER / 8) + u, rW, rX, dma_base);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto slot_of = [&](auto s_) -> const u32x4* {
-    constexpr int S = decltype(s_)::value & 3;
-    if constexpr (S == 0) return L0;
-    else if constexpr (S == 1) return L1;
-    else if constexpr (S == 2) return L2;
-    else return L3;
-  };
   const i32x4 none{0, 0, 0, 0};
   auto stage = [&](int kt, auto s_) {
-    using S = decltype(s_);
-    const u32x4* cur = slot_of(s_);
-    kstep(fr0, fr1, cur, 1, false, none, none, 0);
-    wait_vmcnt<2 * PER>();  // stage kt+1 landed (kt+2, kt+3 may still be in flight)
-    lds_barrier();
-    kstep(fr1, fr0, slot_of(std::integral_constant<int, S::value + 1>{}), 0, true, rsrc_w(kt + 4), rsrc_x(kt + 4),
-          base[S::value & 3]);
+    constexpr int S = decltype(s_)::value % NS;
+    const u32x4* cur = ring + S * C::SLOT;
+#pragma unroll
+    for (int ks = 0; ks + 1 < C::KS; ++ks) {
+      if (ks % 2 == 0) kstep(fr0, fr1, cur, ks + 1, false, none, none, 0);
+      else kstep(fr1, fr0, cur, ks + 1, false, none, none, 0);
+    }
+    // stage kt+1 has landed once at most this wave's DMAs of stage kt+2 are
+    // outstanding; after the barrier that holds for every wave, and every
+    // wave has finished stage kt-1 (its fragment reads completed before its
+    // MFMAs ran), so that slot takes stage kt+NS-1.  The reads of stage kt
+    // still in flight need no wait: nothing overwrites its slot now.
+    wait_vmcnt<(NS - 3) * C::PER>();
+    barrier_only();
+    const u32x4* nxt = ring + ((S + 1) % NS) * C::SLOT;
+    kstep(fr1, fr0, nxt, 0, true, rsrc_w(kt + NS - 1), rsrc_x(kt + NS - 1),
+          ring_base + (uint32_t)(((S + NS - 1) % NS) * C::SLOT * 16));
   };
+
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) {
+    const i32x4 rW = rsrc_w(st), rX = rsrc_x(st);
+#pragma unroll
+    for (int i = 0; i < C::PER; ++i) dma(i, rW, rX, ring_base + (uint32_t)(st * C::SLOT * 16));
+  }
+  wait_vmcnt<(NS - 2) * C::PER>();
+  lds_barrier();
+#pragma unroll
+  for (int r = 0; r < 8; ++r) fr0[r] = __builtin_bit_cast(bf16x8, ring[frag_addr(r, 0)]);
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
-
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const i32x4 rW = rsrc_w(s), rX = rsrc_x(s);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) dma(i, rW, rX, base[s]);
-  }
-  wait_vmcnt<3 * PER>();
-  lds_barrier();
-#pragma unroll
-  for (int r = 0; r < 8; ++r) fr0[r] = __builtin_bit_cast(bf16x8, L0[frag_addr(r, 0)]);
   int kt = 0;
-  for (; kt + 4 <= nk; kt += 4) {
-    stage(kt, I0{});
-    stage(kt + 1, I1{});
-    stage(kt + 2, I2{});
-    stage(kt + 3, I3{});
+  if constexpr (NS == 4) {
+    for (; kt + 4 <= nk; kt += 4) {
+      stage(kt, I0{});
+      stage(kt + 1, I1{});
+      stage(kt + 2, I2{});
+      stage(kt + 3, I3{});
+    }
+    if (kt < nk) {  // nk is even: at most two stages remain (slots 0, 1)
+      stage(kt, I0{});
+      stage(kt + 1, I1{});
+    }
+  } else {
+    static_assert(NS == 4, "ring of four slots");
   }
-  if (kt < nk) {  // K is a multiple of 64: at most two stages remain (slots 0, 1)
-    stage(kt, I0{});
-    stage(kt + 1, I1{});
-  }
-  wait_vmcnt<0>();  // the empty DMAs issued past the end have retired
+  wait_vmcnt<0>();
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -740,15 +750,16 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
-  using C = BigCfg;
+  constexpr int CPR = 4, NS = 4;
+  using C = BigCfg<CPR, NS>;
   if (a.N % C::BN != 0 || a.K % (2 * C::BK) != 0 || a.M <= 0) return hipErrorInvalidValue;
   if ((int64_t)C::BN * a.K * 2 >= (1ll << 31) || (int64_t)C::BM * a.ldx * 2 >= (1ll << 31)) return hipErrorInvalidValue;
   const int grid = (a.N / C::BN) * ((a.M + C::BM - 1) / C::BM);
   switch (a.epi) {
-    case Epi::QKV: gemm_big_kernel<0><<<grid, C::NT, 0, s>>>(a); break;
-    case Epi::RESID_H: gemm_big_kernel<1><<<grid, C::NT, 0, s>>>(a); break;
-    case Epi::SWIGLU: gemm_big_kernel<2><<<grid, C::NT, 0, s>>>(a); break;
-    case Epi::RESID_OUT: gemm_big_kernel<3><<<grid, C::NT, 0, s>>>(a); break;
+    case Epi::QKV: gemm_big_kernel<0, CPR, NS><<<grid, C::NT, 0, s>>>(a); break;
+    case Epi::RESID_H: gemm_big_kernel<1, CPR, NS><<<grid, C::NT, 0, s>>>(a); break;
+    case Epi::SWIGLU: gemm_big_kernel<2, CPR, NS><<<grid, C::NT, 0, s>>>(a); break;
+    case Epi::RESID_OUT: gemm_big_kernel<3, CPR, NS><<<grid, C::NT, 0, s>>>(a); break;
   }
   return hipGetLastError();
 }
