@@ -404,9 +404,13 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* _
     for (int e = 0; e < D / 64; ++e) acc[e] += f * ps[2 + lane + 64 * e];
   }
   const float inv = 1.f / L;
-  T* out = attn + (size_t)b * H * D + (size_t)h * D;
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = from_f32<T>(acc[e] * inv);
+  for (int e = 0; e < D / 64; ++e) {
+    const int col = h * D + lane + 64 * e;
+    // bf16: the o_proj GEMM's tiled operand; fp32: row-major [B][H*D]
+    const size_t o = sizeof(T) == 2 ? tiled_off(b, col, H * D) : (size_t)b * H * D + col;
+    attn[o] = from_f32<T>(acc[e] * inv);
+  }
 }
 
 template <typename T, int D>

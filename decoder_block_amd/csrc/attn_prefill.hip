@@ -357,15 +357,16 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
     const int j = wave * 32 * C::RB + 32 * x + (lane & 31);
     const float l_tot = l_run[x] + __shfl_xor(l_run[x], 32, 64);
     const float inv = 1.f / l_tot;
-    T* op = attn + ((size_t)b * S + row_sidx(j)) * HD + (size_t)row_head(j) * D;
+    const int tok = b * S + row_sidx(j), col0 = row_head(j) * D;
+    T* op = attn + (size_t)tok * HD + col0;  // fp32: row-major [B*S][H*D]
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
       for (int ig = 0; ig < 4; ++ig) {
         const int d0 = 32 * db + 8 * ig + 4 * hl;
         const f32x16& ov = o[x][db];
-        if constexpr (sizeof(T) == 2) {
-          *reinterpret_cast<bf16x4*>(op + d0) =
+        if constexpr (sizeof(T) == 2) {  // bf16: the o_proj GEMM's tiled operand
+          *reinterpret_cast<bf16x4*>(attn + tiled_off(tok, col0 + d0, HD)) =
               bf16x4{from_f32<bf16>(ov[4 * ig] * inv), from_f32<bf16>(ov[4 * ig + 1] * inv),
                      from_f32<bf16>(ov[4 * ig + 2] * inv), from_f32<bf16>(ov[4 * ig + 3] * inv)};
         } else {

@@ -163,3 +163,16 @@ __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 DEVI float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
 template <typename T> DEVI T ceil_div(T a, T b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Tiled storage of bf16 GEMM operands (packed weights and the activations the
+// layer's own kernels produce for a GEMM): blocks of 256 rows x 32 columns
+// (16 KB, row-major inside), ordered by row block, then column block.  One
+// 32-deep K stage of a 256-row tile is then one contiguous 16 KB piece, so its
+// LDS DMAs fetch whole cache lines.  K is a multiple of 32; storage holds the
+// row count rounded up to 256.  Returns the element offset of (r, k).
+// ---------------------------------------------------------------------------
+constexpr int kTileRows = 256, kTileCols = 32, kTileElems = kTileRows * kTileCols;
+DEVI size_t tiled_off(int r, int k, int K) {
+  return ((size_t)(r >> 8) * (size_t)(K >> 5) + (size_t)(k >> 5)) * kTileElems + (size_t)((r & 255) * 32 + (k & 31));
+}

@@ -25,6 +25,13 @@
 // reads never wait for the DMAs of other stages.  The workgroup -> tile map
 // keeps the tiles that share weight panels on one XCD (8 XCDs, each with its
 // own L2).
+//
+// bf16 operands (packed weights and the activations the layer writes for a
+// GEMM) are stored in 256-row x 32-column tiles (tiled_off): a stage of a tile
+// is then one contiguous piece of 64-byte rows, and its DMAs fetch whole
+// 128-byte lines.  With row-major operands a 32-deep stage touches half of
+// every line of its rows, and the DMA stream into LDS was measured at about
+// 60% of the rate for whole lines; that stream set the GEMMs' speed.
 #include "common.h"
 #include "kernels.h"
 #include <algorithm>
@@ -124,7 +131,9 @@ DEVI void epilogue(const GemmArgs& a, int t, int f, f32x4 v) {
     v *= r;
     const float s0 = silu(v[0]) * v[1];
     const float s1 = silu(v[2]) * v[3];
-    T* o = reinterpret_cast<T*>(a.out) + (size_t)t * a.ldo + f / 2;
+    // s columns f/2, f/2 + 1 (f/2 even: one tile row of the down GEMM's operand)
+    T* o = reinterpret_cast<T*>(a.out) +
+           (sizeof(T) == 2 ? tiled_off(t, f / 2, a.ldo) : (size_t)t * a.ldo + f / 2);
     o[0] = from_f32<T>(s0);
     o[1] = from_f32<T>(s1);
   } else {  // RESID_OUT
@@ -176,26 +185,34 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   // lane loads exactly that chunk (the swizzle is its own inverse).  Rows of X
   // past M fall outside the buffer's range and arrive as zeros.
   constexpr int ES = (int)sizeof(T);
+  // bf16 operands are tiled: a stage of BN (BM) rows is one contiguous piece
+  // of 64-byte rows inside a 256 x 32 tile, the next stage 16 KB further.
+  // fp32 operands are row-major with pitch K (W) and ldx (X).
+  constexpr bool TILED = sizeof(T) == 2;
   int vW[C::LW], vX[C::LX];
 #pragma unroll
   for (int i = 0; i < C::LW; ++i) {
     const int slot = (wave * C::LW + i) * 64 + lane;
     const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
-    vW[i] = (row * a.K + c * Chunk<T>::N) * ES;
+    vW[i] = TILED ? row * 64 + c * 16 : (row * a.K + c * Chunk<T>::N) * ES;
   }
 #pragma unroll
   for (int i = 0; i < C::LX; ++i) {
     const int slot = (wave * C::LX + i) * 64 + lane;
     const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
-    vX[i] = (row * a.ldx + c * Chunk<T>::N) * ES;
+    vX[i] = TILED ? row * 64 + c * 16 : (row * a.ldx + c * Chunk<T>::N) * ES;
   }
-  const char* Wt = reinterpret_cast<const char*>(a.W) + (size_t)n0 * a.K * ES;
-  const char* Xt = reinterpret_cast<const char*>(a.X) + (size_t)m0 * a.ldx * ES;
+  const char* Wt = reinterpret_cast<const char*>(a.W) +
+                   (TILED ? tiled_off(n0, 0, a.K) * ES : (size_t)n0 * a.K * ES);
+  const char* Xt = reinterpret_cast<const char*>(a.X) +
+                   (TILED ? tiled_off(m0, 0, a.K) * ES : (size_t)m0 * a.ldx * ES);
   // bytes of X from the tile's first row to the end of the matrix (< 2^31 for
-  // every supported shape), kept wave-uniform so the descriptor lives in SGPRs
-  const uint64_t xb = (uint64_t)(a.M - m0) * (uint64_t)a.ldx * ES;
+  // every supported shape), kept wave-uniform so the descriptor lives in SGPRs;
+  // tiled X holds whole 256-row tiles, so a stage never reads past them
+  const uint64_t xb = TILED ? (uint64_t)C::BM * 64 : (uint64_t)(a.M - m0) * (uint64_t)a.ldx * ES;
   const int x_bytes = __builtin_amdgcn_readfirstlane((int)(xb < 0x7fffffffull ? xb : 0x7fffffffull));
   const int nk = a.K / C::BK;
+  constexpr int STAGE_BYTES = TILED ? kTileElems * 2 : C::BK * ES;  // distance between stages
 
   auto slot_of = [&](auto s_) -> u32x4* {
     constexpr int S = decltype(s_)::value & 3;
@@ -209,9 +226,9 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   // stage waits with the same count.
   auto issue = [&](int kt, u32x4* L) {
     const bool live = kt < nk;
-    const int kb = live ? kt * C::BK * ES : 0;
-    const i32x4 rW = make_rsrc(Wt + kb, live ? 0x7fffffffu : 0u);
-    const i32x4 rX = make_rsrc(Xt + kb, live ? (uint32_t)(x_bytes - kb) : 0u);
+    const int kb = live ? kt * STAGE_BYTES : 0;
+    const i32x4 rW = make_rsrc(Wt + kb, live ? (TILED ? (uint32_t)C::BN * 64 : 0x7fffffffu) : 0u);
+    const i32x4 rX = make_rsrc(Xt + kb, live ? (uint32_t)(TILED ? x_bytes : x_bytes - kb) : 0u);
 #pragma unroll
     for (int i = 0; i < C::LW; ++i) buf_dma16_async(rW, L + (wave * C::LW + i) * 64, vW[i]);
 #pragma unroll
@@ -338,30 +355,32 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
 
-  constexpr int ES = 2;
+  // W and X are tiled (256 x 32 tiles): the tile's stage kt is one 16 KB piece
+  // of 64-byte rows for W and one for X, so every DMA fetches whole cache lines.
+  // A lane's 16 bytes sit at the same offset inside every stage.
+  static_assert(C::BK == kTileCols, "one tile column block per stage");
+  constexpr int STAGE_BYTES = kTileElems * 2;
   int voff[C::PER];
 #pragma unroll
   for (int i = 0; i < C::PER; ++i) {
     const int slot = (wave * C::PER + i) * 64 + lane;
     const int row = slot / C::CPR;
     const int c = C::swz(row, slot % C::CPR) - row * C::CPR;
-    voff[i] = row < C::BN ? (row * a.K + 8 * c) * ES : ((row - C::BN) * a.ldx + 8 * c) * ES;
+    voff[i] = (row < C::BN ? row : row - C::BN) * 64 + 16 * c;
   }
-  const char* Wt = reinterpret_cast<const char*>(a.W) + (size_t)n0 * a.K * ES;
-  const char* Xt = reinterpret_cast<const char*>(a.X) + (size_t)m0 * a.ldx * ES;
-  const uint64_t xb = (uint64_t)(a.M - m0) * (uint64_t)a.ldx * ES;
-  const int x_bytes = __builtin_amdgcn_readfirstlane((int)(xb < 0x7fffffffull ? xb : 0x7fffffffull));
+  const char* Wt = reinterpret_cast<const char*>(a.W) + tiled_off(n0, 0, a.K) * 2;
+  const char* Xt = reinterpret_cast<const char*>(a.X) + tiled_off(m0, 0, a.K) * 2;
   const int nk = a.K / C::BK;
   const uint32_t ring_base = lds_address(ring);
 
+  // stages past the end get an empty range: no memory moves, same DMA count
   auto rsrc_w = [&](int kt) {
     const bool live = kt < nk;
-    return make_rsrc(Wt + (live ? kt * C::BK * ES : 0), live ? 0x7fffffffu : 0u);
+    return make_rsrc(Wt + (live ? kt * STAGE_BYTES : 0), live ? (uint32_t)STAGE_BYTES : 0u);
   };
   auto rsrc_x = [&](int kt) {
     const bool live = kt < nk;
-    const int kb = live ? kt * C::BK * ES : 0;
-    return make_rsrc(Xt + kb, live ? (uint32_t)(x_bytes - kb) : 0u);
+    return make_rsrc(Xt + (live ? kt * STAGE_BYTES : 0), live ? (uint32_t)STAGE_BYTES : 0u);
   };
   auto dma = [&](int i, const i32x4& rW, const i32x4& rX, uint32_t slot_base) {
     const int q = wave * C::PER + i;  // DMA group: W rows while q * 64 < BN * CPR
@@ -473,128 +492,19 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // Skinny bf16 GEMM for few tokens (decode): the weights are streamed once from
 // HBM and the work is bound by that stream, so the shape is chosen for memory
-// parallelism, not reuse.  A workgroup owns 64 features x 64 tokens and one
-// of KS slices of K; each of its four waves walks a quarter of the slice on
-// its own (no barriers in the main loop), loading W and X fragments straight
-// into registers through buffer descriptors (X rows past M read as zeros),
-// three k-steps ahead of the MFMAs.  The four waves add their tiles through
-// LDS; with KS = 1 the epilogue runs directly, otherwise the fp32 partial
-// goes to [ks][M][N] and a second pass adds the KS partials in a fixed order
-// and runs the epilogue.
+// parallelism, not reuse.  One workgroup per CU, each owning 64 features x 64
+// tokens and one of KS slices of K.  K is split into the largest power of two
+// of slices that keeps the workgroups within one round of the 256 CUs (each
+// further round pays the pipeline ramp-up again), with at least two 64-deep
+// stages per slice.  With KS = 1 the epilogue runs directly, otherwise the
+// fp32 partial goes to [ks][M][N] and a second pass adds the KS partials in a
+// fixed order and runs the epilogue.
 // ---------------------------------------------------------------------------
-constexpr int kSkinnyTargetGroups = 512;
-
-// K % 64 == 0: the LDS-staged streaming kernel, one workgroup per CU.  K is
-// split into the largest power of two of slices that keeps the workgroups
-// within one round of the 256 CUs (each further round pays the pipeline
-// ramp-up again), and at least two stages per slice.
-bool skinny_streams(int K) { return K % 64 == 0; }
-
 int skinny_ks(int M, int N, int K) {
   const int groups = (N / 64) * ((M + 63) / 64);
-  if (skinny_streams(K)) {
-    int ks = 1;
-    while (ks < 16 && groups * ks * 2 <= 256 && K / (128 * ks * 2) >= 1) ks *= 2;
-    return ks;
-  }
-  int ks = (kSkinnyTargetGroups + groups - 1) / groups;
-  ks = std::min(ks, 8);
-  ks = std::min(ks, std::max(1, K / 128));  // every wave keeps at least one 32-deep k-step
-  return std::max(ks, 1);
-}
-
-template <int EPI>
-__global__ __launch_bounds__(256, 2) void gemm_skinny_kernel(GemmArgs a, int KS) {
-  constexpr int RS = 68;  // LDS row stride (floats) of the reduction tile
-  __shared__ float red[4][64 * RS];
-  const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64, ks = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c16 = lane & 15, g4 = lane >> 4;
-
-  const int nk = a.K / 32;
-  const int g_beg = nk * ks / KS, g_end = nk * (ks + 1) / KS;
-  const int w_beg = g_beg + (g_end - g_beg) * wave / 4, w_end = g_beg + (g_end - g_beg) * (wave + 1) / 4;
-
-  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(static_cast<const void*>(static_cast<const bf16*>(a.W) + (size_t)n0 * a.K)), 0,
-      64 * a.K * 2, 0x00020000);
-  const int x_rows = min(64, a.M - m0);
-  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<void*>(static_cast<const void*>(static_cast<const bf16*>(a.X) + (size_t)m0 * a.ldx)), 0,
-      x_rows * a.ldx * 2, 0x00020000);
-  int vw[4], vx[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    vw[i] = ((16 * i + c16) * a.K + 8 * g4) * 2;
-    vx[i] = ((16 * i + c16) * a.ldx + 8 * g4) * 2;
-  }
-  struct Frag {
-    bf16x8 w[4], x[4];
-  };
-  // k-steps past the wave's range move their (range-checked) VGPR offset past
-  // num_records (< 2^30 by the launch check), so they read zeros without traffic
-  auto load = [&](Frag& f, int kt) {
-    const int ko = kt < w_end ? kt * 64 : (1 << 30);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      f.w[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rw, vw[i] + ko, 0, 0));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      f.x[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rx, vx[j] + ko, 0, 0));
-  };
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto mma = [&](const Frag& f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma16_chunk(acc[i][j], f.w[i], f.x[j]);
-  };
-  if (w_beg < w_end) {
-    Frag f0, f1, f2;
-    load(f0, w_beg);
-    load(f1, w_beg + 1);
-#pragma unroll 1
-    for (int kt = w_beg; kt < w_end; kt += 3) {
-      load(f2, kt + 2);
-      mma(f0);
-      load(f0, kt + 3);
-      if (kt + 1 < w_end) mma(f1);
-      load(f1, kt + 4);
-      if (kt + 2 < w_end) mma(f2);
-    }
-  }
-
-  // add the four waves' tiles: red[w][feature][token]
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) red[wave][(16 * i + 4 * g4 + e) * RS + 16 * j + c16] = acc[i][j][e];
-  __syncthreads();
-  const int tt = tid & 63, fg = tid >> 6;  // token, group of 16 features
-  const int t = m0 + tt;
-  if (t >= a.M) return;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    f32x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = (16 * fg + 4 * u + e) * RS + tt;
-      v[e] = (red[0][r] + red[1][r]) + (red[2][r] + red[3][r]);
-    }
-    const int f = n0 + 16 * fg + 4 * u;
-    if (KS == 1) {
-      epilogue<bf16, EPI>(a, t, f, v);
-    } else {
-      *reinterpret_cast<f32x4*>(a.split_ws + ((size_t)ks * a.M + t) * a.N + f) = v;
-    }
-  }
+  int ks = 1;
+  while (ks < 16 && groups * ks * 2 <= 256 && K / (128 * ks * 2) >= 1) ks *= 2;
+  return ks;
 }
 
 template <int EPI>
@@ -641,10 +551,14 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a, int KS) {
   const int s_beg = nk * ks / KS, s_end = nk * (ks + 1) / KS;
   const int ns = s_end - s_beg;
 
+  // W and X are tiled (256 x 32 tiles): a 64-deep stage of 64 rows is two
+  // contiguous 4 KB pieces, one in each of two consecutive tile column blocks
+  // (16 KB apart).  X rows past M are padding rows of the tile (never stored).
   // DMA i of this thread: chunk slot (wave * PER + i) * 64 + lane of a stage
-  const char* Wt = reinterpret_cast<const char*>(a.W) + ((size_t)n0 * a.K + (size_t)s_beg * 64) * 2;
-  const char* Xt = reinterpret_cast<const char*>(a.X) + ((size_t)m0 * a.ldx + (size_t)s_beg * 64) * 2;
-  const int x_rows = min(64, a.M - m0);
+  const char* Wt = reinterpret_cast<const char*>(a.W) + tiled_off(n0, s_beg * 64, a.K) * 2;
+  const char* Xt = reinterpret_cast<const char*>(a.X) + tiled_off(m0, s_beg * 64, a.K) * 2;
+  constexpr int STAGE_BYTES = 2 * kTileElems * 2;
+  constexpr uint32_t RANGE = kTileElems * 2 + 64 * 64;  // both 4 KB pieces
   // DMA group q = wave * PER + i covers rows 8q .. 8q + 7: W rows for q < 8,
   // X rows after (wave-uniform, so the descriptor choice stays scalar)
   int voff[C::PER];
@@ -652,14 +566,14 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a, int KS) {
   for (int i = 0; i < C::PER; ++i) {
     const int slot = (wave * C::PER + i) * 64 + lane;
     const int row = slot / C::CPR, c = (slot % C::CPR) ^ (row & 7);
-    voff[i] = row >= 64 ? ((row - 64) * a.ldx + 8 * c) * 2 : (row * a.K + 8 * c) * 2;
+    voff[i] = (c >> 2) * kTileElems * 2 + (row & 63) * 64 + (c & 3) * 16;
   }
   const uint32_t ring_base = lds_address(ring);
   auto issue = [&](int st) {
     const bool live = st < ns;
-    const int kb = live ? st * 128 : 0;
-    const i32x4 rW = make_rsrc(Wt + kb, live ? (uint32_t)(64 * a.K * 2) : 0u);
-    const i32x4 rX = make_rsrc(Xt + kb, live ? (uint32_t)(x_rows * a.ldx * 2) : 0u);
+    const int kb = live ? st * STAGE_BYTES : 0;
+    const i32x4 rW = make_rsrc(Wt + kb, live ? RANGE : 0u);
+    const i32x4 rX = make_rsrc(Xt + kb, live ? RANGE : 0u);
     const uint32_t slot_base = ring_base + (uint32_t)((st % C::NSL) * C::SLOT * 16);
 #pragma unroll
     for (int i = 0; i < C::PER; ++i)
@@ -706,10 +620,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a, int KS) {
 template <int EPI>
 hipError_t launch_skinny_epi(const GemmArgs& a, int KS, hipStream_t s) {
   dim3 grid(a.N / 64, (a.M + 63) / 64, KS);
-  if (skinny_streams(a.K))
-    gemm_stream_kernel<EPI><<<grid, 256, 0, s>>>(a, KS);
-  else
-    gemm_skinny_kernel<EPI><<<grid, 256, 0, s>>>(a, KS);
+  gemm_stream_kernel<EPI><<<grid, 256, 0, s>>>(a, KS);
   if (KS > 1) {
     const size_t n = (size_t)a.M * (a.N / 4);
     gemm_split_reduce_kernel<EPI><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, KS);
@@ -718,8 +629,7 @@ hipError_t launch_skinny_epi(const GemmArgs& a, int KS, hipStream_t s) {
 }
 
 hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
-  if (a.N % 64 != 0 || a.K % 32 != 0 || a.M <= 0) return hipErrorInvalidValue;
-  if ((int64_t)64 * a.K * 2 >= (1ll << 30) || (int64_t)64 * a.ldx * 2 >= (1ll << 30)) return hipErrorInvalidValue;
+  if (a.N % 64 != 0 || a.K % 64 != 0 || a.M <= 0 || a.M > 256) return hipErrorInvalidValue;
   const int KS = skinny_ks(a.M, a.N, a.K);
   if (KS > 1 && (a.split_ws == nullptr || a.split_ws_bytes < (size_t)KS * a.M * a.N * sizeof(float)))
     return hipErrorInvalidValue;
@@ -735,9 +645,10 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
 template <typename T, typename C>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   if (a.N % C::BN != 0 || a.K % (2 * C::BK) != 0 || a.M <= 0) return hipErrorInvalidValue;
-  // 32-bit buffer offsets: a tile's rows times the row pitch must stay below 2^31
-  if ((int64_t)C::BN * a.K * (int64_t)sizeof(T) >= (1ll << 31) ||
-      (int64_t)C::BM * a.ldx * (int64_t)sizeof(T) >= (1ll << 31))
+  // row-major (fp32) operands: 32-bit buffer offsets, so a tile's rows times
+  // the row pitch must stay below 2^31 (tiled bf16 stages are 16 KB pieces)
+  if (sizeof(T) == 4 && ((int64_t)C::BN * a.K * (int64_t)sizeof(T) >= (1ll << 31) ||
+                         (int64_t)C::BM * a.ldx * (int64_t)sizeof(T) >= (1ll << 31)))
     return hipErrorInvalidValue;
   const int grid = (a.N / C::BN) * ((a.M + C::BM - 1) / C::BM);
   switch (a.epi) {
@@ -753,7 +664,6 @@ hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
   constexpr int CPR = 4, NS = 4;
   using C = BigCfg<CPR, NS>;
   if (a.N % C::BN != 0 || a.K % (2 * C::BK) != 0 || a.M <= 0) return hipErrorInvalidValue;
-  if ((int64_t)C::BN * a.K * 2 >= (1ll << 31) || (int64_t)C::BM * a.ldx * 2 >= (1ll << 31)) return hipErrorInvalidValue;
   const int grid = (a.N / C::BN) * ((a.M + C::BM - 1) / C::BM);
   switch (a.epi) {
     case Epi::QKV: gemm_big_kernel<0, CPR, NS><<<grid, C::NT, 0, s>>>(a); break;

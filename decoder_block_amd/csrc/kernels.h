@@ -32,9 +32,12 @@ struct CacheView {
 
 enum class Epi : int { QKV = 0, RESID_H = 1, SWIGLU = 2, RESID_OUT = 3 };
 
+// bf16 operands are stored in 256 x 32 tiles (tiled_off in common.h): the
+// packed weights with N rounded up to 256 rows, the activations with M rounded
+// up to 256 rows.  fp32 operands are row-major.
 struct GemmArgs {
-  const void* W;  // packed weights [N][K] (features x K), K-contiguous
-  const void* X;  // activations [M][ldx], K-contiguous
+  const void* W;  // packed weights [N][K] (features x K): bf16 tiled, fp32 row-major
+  const void* X;  // activations [M][K]: bf16 tiled; fp32 row-major with pitch ldx
   int M, N, K, ldx;
   Epi epi;
   const float* rowscale;  // QKV / SWIGLU: per-token RMSNorm scale
@@ -47,7 +50,7 @@ struct GemmArgs {
   int H;
   // residual / output epilogues
   const void* resid;  // RESID_H: x [M][N] (layer dtype); RESID_OUT: h [M][N] fp32
-  void* out;          // RESID_H: h fp32; SWIGLU: s [M][ldo]; RESID_OUT: out
+  void* out;          // RESID_H: h fp32; SWIGLU: s [M][ldo] (bf16 tiled); RESID_OUT: out
   int ldo;
   DType out_dtype;    // RESID_OUT only
   // SKINNY tiles split K over workgroups; their fp32 partial sums [ks][M][N]
@@ -67,24 +70,26 @@ size_t skinny_partial_bytes(int M, int N, int K);
 
 hipError_t launch_gemm(DType t, GemmTile tile, const GemmArgs& a, hipStream_t s);
 
-// RMSNorm row scale r[t] = rsqrt(mean(x[t]^2) + eps) of x [M][d] (layer dtype).
+// RMSNorm row scale r[t] = rsqrt(mean(x[t]^2) + eps) of x [M][d] (layer dtype),
+// plus (bf16, xt non-null) a tiled copy of x as the QKV GEMM operand.
 struct Upload;
 // `up` (may be null) is a batch of int32 stores applied by the same launch
 // before any later kernel on the stream runs (host bookkeeping of the step).
-hipError_t launch_rms_rowscale(DType t, const void* x, float* r, int M, int d, float eps, const Upload* up,
-                               hipStream_t s);
+hipError_t launch_rms_rowscale(DType t, const void* x, float* r, void* xt, int M, int d, float eps,
+                               const Upload* up, hipStream_t s);
 // Second norm: r2[t] from h [M][d] fp32, plus hb = h * gamma (fp32 gamma) rounded
-// once to the layer dtype.
+// once to the layer dtype (bf16: tiled).
 hipError_t launch_rms_convert(DType t, const float* h, const float* gamma, void* hb, float* r,
                               int M, int d, float eps, hipStream_t s);
 
-// Causal GQA prefill attention: q [B*S][H*D] -> attn [B*S][H*D], keys from the cache.
+// Causal GQA prefill attention: q [B*S][H*D] -> attn [B*S][H*D] (bf16 tiled),
+// keys from the cache.
 hipError_t launch_attn_prefill(DType t, const void* q, void* attn, int H, const CacheView& c,
                                const BatchView& b, hipStream_t s);
 
 // Split-K paged decode attention.  partial: [B][H][max_splits][D + 2] fp32
 // holding (running max, sum, unnormalised output) per key chunk; the combine
-// kernel merges the chunks into attn [B][H*D].
+// kernel merges the chunks into attn [B][H*D] (bf16 tiled).
 int decode_split_keys();
 hipError_t launch_attn_decode(DType t, const void* q, float* partial, int max_splits, int H,
                               const CacheView& c, const BatchView& b, hipStream_t s);
@@ -92,8 +97,9 @@ hipError_t launch_attn_decode_combine(DType t, const float* partial, void* attn,
                                       int H, int D, const BatchView& b, hipStream_t s);
 
 // Weight packing.  dst[r][c] = src[r][c] * (gamma ? gamma[c] : 1) for r < rows,
-// c < cols; padded columns up to ldd and padded rows up to rows_pad are zero.
-// Row r of the source lands at dst row (r * row_mul + row_add).
+// c < cols, with ldd columns (bf16: tiled, fp32: row-major); the caller zeroes
+// the buffer first, so padded rows and columns stay zero.  Row r of the source
+// lands at dst row (r * row_mul + row_add).
 hipError_t launch_pack(DType t, const void* src, const void* gamma, void* dst, int rows,
                        int cols, int ldd, int row_mul, int row_add, hipStream_t s);
 hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s);

@@ -37,9 +37,14 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 struct Shape {
   int d, I, I_pad, H, G, D, HD, KD, NQKV, NQKV_pad, max_pos;
+  int d_rows;  // stored rows of W_o and W_down: d, rounded up to 256 for tiled bf16
   DType dt;
   size_t es;
 };
+
+// bf16 GEMM operands are stored in 256-row tiles: activation buffers hold the
+// token count rounded up to 256 rows
+size_t op_rows(const Shape& s, size_t T) { return s.dt == DType::BF16 ? (T + 255) / 256 * 256 : T; }
 
 llama_status check_config(const llama_layer_config* c, Shape* s) {
   if (!c) return LLAMA_ERR_INVALID_ARG;
@@ -76,6 +81,7 @@ llama_status check_config(const llama_layer_config* c, Shape* s) {
   s->max_pos = c->max_position;
   s->dt = c->dtype == LLAMA_DTYPE_BF16 ? DType::BF16 : DType::F32;
   s->es = llk::dsize(s->dt);
+  s->d_rows = s->dt == DType::BF16 ? (s->d + 255) / 256 * 256 : s->d;
   return LLAMA_OK;
 }
 
@@ -89,11 +95,11 @@ PackedLayout packed_layout(const Shape& s) {
   p.qkv = off;
   off = align256(off + (size_t)s.NQKV_pad * s.d * s.es);
   p.o = off;
-  off = align256(off + (size_t)s.d * s.HD * s.es);
+  off = align256(off + (size_t)s.d_rows * s.HD * s.es);
   p.gu = off;
   off = align256(off + (size_t)2 * s.I_pad * s.d * s.es);
   p.down = off;
-  off = align256(off + (size_t)s.d * s.I_pad * s.es);
+  off = align256(off + (size_t)s.d_rows * s.I_pad * s.es);
   p.gamma2 = off;
   off = align256(off + (size_t)s.d * sizeof(float));
   p.cos = off;
@@ -107,7 +113,7 @@ PackedLayout packed_layout(const Shape& s) {
 int max_splits_for(const Shape& s) { return (s.max_pos + llk::decode_split_keys() - 1) / llk::decode_split_keys(); }
 
 struct WsLayout {
-  size_t desc, r1, r2, q, attn, h, hb, s, part, gpart, gpart_bytes, total;
+  size_t desc, r1, r2, xt, q, attn, h, hb, s, part, gpart, gpart_bytes, total;
 };
 
 bool use_skinny(const Shape& sh, long M) { return sh.dt == DType::BF16 && M <= 128; }
@@ -135,16 +141,19 @@ WsLayout ws_layout(const Shape& sh, size_t T, size_t B) {
   off = align256(off + T * sizeof(float));
   w.r2 = off;
   off = align256(off + T * sizeof(float));
+  const size_t Tp = op_rows(sh, T);  // GEMM operands: whole 256-row tiles (bf16)
+  w.xt = off;
+  off = align256(off + (sh.dt == DType::BF16 ? Tp * sh.d * sh.es : 0));
   w.q = off;
   off = align256(off + T * sh.HD * sh.es);
   w.attn = off;
-  off = align256(off + T * sh.HD * sh.es);
+  off = align256(off + Tp * sh.HD * sh.es);
   w.h = off;
   off = align256(off + T * sh.d * sizeof(float));
   w.hb = off;
-  off = align256(off + T * sh.d * sh.es);
+  off = align256(off + Tp * sh.d * sh.es);
   w.s = off;
-  off = align256(off + T * sh.I_pad * sh.es);
+  off = align256(off + Tp * sh.I_pad * sh.es);
   w.part = off;
   off = align256(off + B * sh.H * (size_t)max_splits_for(sh) * (sh.D + 2) * sizeof(float));
   w.gpart = off;
@@ -672,6 +681,7 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
 
   float* r1 = reinterpret_cast<float*>(W + wl.r1);
   float* r2 = reinterpret_cast<float*>(W + wl.r2);
+  void* xt = s.dt == DType::BF16 ? W + wl.xt : nullptr;  // tiled copy of x (QKV operand)
   void* qb = W + wl.q;
   void* attn = W + wl.attn;
   float* h = reinterpret_cast<float*>(W + wl.h);
@@ -695,14 +705,15 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
                  batch, seq_len, M, s.d, s.H, s.G, s.D, s.I);
 
   // RMSNorm_1 statistics
-  HIP_TRY(timed(L, K_RMS1, hs, [&] { return llk::launch_rms_rowscale(s.dt, x, r1, M, s.d, eps, last_upload, hs); }));
+  HIP_TRY(timed(L, K_RMS1, hs,
+                [&] { return llk::launch_rms_rowscale(s.dt, x, r1, xt, M, s.d, eps, last_upload, hs); }));
 
   // QKV + RoPE + cache append
   llk::GemmArgs a{};
   a.split_ws = gpart;
   a.split_ws_bytes = wl.gpart_bytes;
   a.W = P + L->pl.qkv;
-  a.X = x;
+  a.X = xt ? xt : x;
   a.M = M;
   a.N = s.NQKV_pad;
   a.K = s.d;

@@ -7,7 +7,8 @@ namespace llk {
 namespace {
 
 // dst row (r * row_mul + row_add), columns [0, cols): src[r][c] * gamma[c],
-// computed in fp32 and rounded once to the storage type.
+// computed in fp32 and rounded once to the storage type.  bf16 weights are
+// stored in 256 x 32 tiles (tiled_off, ldd columns); fp32 weights row-major.
 template <typename T>
 __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, const T* __restrict__ gamma,
                                                    T* __restrict__ dst, int rows, int cols, int ldd, int row_mul,
@@ -17,7 +18,11 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, co
     const int r = (int)(i / cols), c = (int)(i % cols);
     float v = to_f32(src[i]);
     if (gamma) v *= to_f32(gamma[c]);
-    dst[(size_t)(r * row_mul + row_add) * ldd + c] = from_f32<T>(v);
+    const int dr = r * row_mul + row_add;
+    if constexpr (sizeof(T) == 2)
+      dst[tiled_off(dr, c, ldd)] = from_f32<T>(v);
+    else
+      dst[(size_t)dr * ldd + c] = from_f32<T>(v);
   }
 }
 

@@ -4,7 +4,8 @@
 // ("Chapter 10: the modern LLaMA architecture", section 4; "3.2 Core
 // components, one by one", 3.2.1).  gamma is folded into the weights of the
 // projection that follows, and the row scale r is applied in that GEMM's
-// epilogue, so the norm itself is one HBM pass that writes 4 bytes per row.
+// epilogue, so the norm itself is one HBM pass that writes 4 bytes per row
+// (bf16 layers also write the GEMM operand in its 256 x 32 tiled order).
 // One wavefront per row, 16-byte loads (eight in flight per lane), shuffle
 // reduction.
 #include "common.h"
@@ -21,7 +22,7 @@ DEVI float wave_sum(float v) {
 
 template <typename T>
 __global__ __launch_bounds__(256) void rms_rowscale_kernel(const T* __restrict__ x, float* __restrict__ r,
-                                                           int M, int d, float eps, Upload u) {
+                                                           T* __restrict__ xt, int M, int d, float eps, Upload u) {
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i < u.n; i += 256) u.base[(u.idx[i] >> 31) & 1][u.idx[i] & 0x7fffffff] = u.val[i];
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -37,6 +38,7 @@ __global__ __launch_bounds__(256) void rms_rowscale_kernel(const T* __restrict__
       const float f = to_f32(v[e]);
       acc += f * f;
     }
+    if constexpr (sizeof(T) == 2) store_chunk<T>(xt + tiled_off(row, c, d), v);  // 8 columns, one tile row
   }
   acc = wave_sum(acc);
   if (lane == 0) r[row] = 1.f / sqrtf(acc / (float)d + eps);
@@ -53,7 +55,6 @@ __global__ __launch_bounds__(256) void rms_convert_kernel(const float* __restric
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
   const float* p = h + (size_t)row * d;
-  T* q = hb + (size_t)row * d;
   float acc = 0.f;
 #pragma unroll 8
   for (int c = lane * 4; c < d; c += 64 * 4) {
@@ -61,9 +62,9 @@ __global__ __launch_bounds__(256) void rms_convert_kernel(const float* __restric
     acc += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
     v *= *reinterpret_cast<const f32x4*>(gamma + c);
     if constexpr (sizeof(T) == 4) {
-      *reinterpret_cast<f32x4*>(q + c) = v;
+      *reinterpret_cast<f32x4*>(hb + (size_t)row * d + c) = v;
     } else {
-      *reinterpret_cast<bf16x4*>(q + c) =
+      *reinterpret_cast<bf16x4*>(hb + tiled_off(row, c, d)) =
           bf16x4{from_f32<bf16>(v[0]), from_f32<bf16>(v[1]), from_f32<bf16>(v[2]), from_f32<bf16>(v[3])};
     }
   }
@@ -73,8 +74,8 @@ __global__ __launch_bounds__(256) void rms_convert_kernel(const float* __restric
 
 }  // namespace
 
-hipError_t launch_rms_rowscale(DType t, const void* x, float* r, int M, int d, float eps, const Upload* up,
-                               hipStream_t s) {
+hipError_t launch_rms_rowscale(DType t, const void* x, float* r, void* xt, int M, int d, float eps,
+                               const Upload* up, hipStream_t s) {
   const int grid = (M + 3) / 4;
   Upload u;
   if (up) {
@@ -83,16 +84,20 @@ hipError_t launch_rms_rowscale(DType t, const void* x, float* r, int M, int d, f
     u.base[0] = u.base[1] = nullptr;
     u.n = 0;
   }
-  if (t == DType::BF16)
-    rms_rowscale_kernel<bf16><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(x), r, M, d, eps, u);
-  else
-    rms_rowscale_kernel<float><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(x), r, M, d, eps, u);
+  if (t == DType::BF16) {
+    if (!xt || d % kTileCols != 0) return hipErrorInvalidValue;
+    rms_rowscale_kernel<bf16><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(x), r, reinterpret_cast<bf16*>(xt),
+                                                   M, d, eps, u);
+  } else {
+    rms_rowscale_kernel<float><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(x), r, nullptr, M, d, eps, u);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_rms_convert(DType t, const float* h, const float* gamma, void* hb, float* r, int M, int d,
                               float eps, hipStream_t s) {
   const int grid = (M + 3) / 4;
+  if (t == DType::BF16 && d % kTileCols != 0) return hipErrorInvalidValue;
   if (t == DType::BF16)
     rms_convert_kernel<bf16><<<grid, 256, 0, s>>>(h, gamma, reinterpret_cast<bf16*>(hb), r, M, d, eps);
   else

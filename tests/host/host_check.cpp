@@ -42,8 +42,11 @@ hipError_t launch_gemm(DType, GemmTile t, const GemmArgs& a, hipStream_t) {
   return hipSuccess;
 }
 hipError_t launch_upload(const Upload& u, hipStream_t);
-hipError_t launch_rms_rowscale(DType, const void*, float*, int, int, float, const Upload* up, hipStream_t s) {
+hipError_t launch_rms_rowscale(DType t, const void*, float*, void* xt, int, int, float, const Upload* up,
+                               hipStream_t s) {
   g_log.push_back("rms1");
+  // bf16 layers get the tiled operand copy of x; fp32 layers read x directly
+  if ((t == DType::BF16) != (xt != nullptr)) g_log.push_back("rms1-xt-mismatch");
   if (up) {  // the batch riding on this launch is applied like a standalone upload
     if (launch_upload(*up, s) != hipSuccess) return hipErrorUnknown;
     --g_uploads;  // not a launch of its own
