@@ -88,7 +88,8 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restr
   const T* vpool = reinterpret_cast<const T*>(cache.v_pool);
   const int32_t* btab = cache.block_table + (size_t)seq * cache.max_blocks;
 
-  const float scale = 1.4426950408889634f / sqrtf((float)D);
+  // q arrives multiplied by log2(e)/sqrt(D) (QKV epilogue): scores are in exp2 units
+  constexpr float scale = 1.f;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[C::NDB];
 #pragma unroll
@@ -233,7 +234,7 @@ constexpr int kWaveKeys = kChunkKeys / 4;
 template <int D>
 struct KV16 {
   bf16x8 k[D / 32];   // K rows: lane (key c16, k-group g4) holds D-chunks 4s + g4
-  u32x2 v[D / 16];    // V^T rows 16 db + c16, keys 4 g4 .. 4 g4 + 3
+  u32x2 v[D / 16];    // V^T rows 16 db + c16, keys 4 g4 .. 4 g4 + 3 (stored at vperm_pos(4 g4))
 };
 
 // Loads of block blk (group g) through buffer descriptors; a block that is not
@@ -253,7 +254,7 @@ DEVI void load_kv16(KV16<D>& r, const bf16* kpool, const bf16* vpool, int blk, b
     r.k[s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, (c16 * D + (4 * s + g4) * 8) * 2, 0, 0));
 #pragma unroll
   for (int db = 0; db < D / 16; ++db)
-    r.v[db] = __builtin_amdgcn_raw_buffer_load_b64(rv, ((16 * db + c16) * 16 + 4 * g4) * 2, 0, 0);
+    r.v[db] = __builtin_amdgcn_raw_buffer_load_b64(rv, ((16 * db + c16) * 16 + vperm_pos(4 * g4)) * 2, 0, 0);
 }
 
 DEVI f32x4 mfma16x16x16(f32x4 c, u32x2 a, u32x2 b) {
@@ -291,7 +292,8 @@ __global__ __launch_bounds__(256, 3) void attn_decode_wave_kernel(const bf16* __
   const bf16* kpool = reinterpret_cast<const bf16*>(cache.k_pool);
   const bf16* vpool = reinterpret_cast<const bf16*>(cache.v_pool);
 
-  const float scale = 1.4426950408889634f / sqrtf((float)D);
+  // q arrives multiplied by log2(e)/sqrt(D) (QKV epilogue): scores are in exp2 units
+  constexpr float scale = 1.f;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[D / 16];
 #pragma unroll

@@ -22,10 +22,12 @@
 //   tile; the row max needs one exchange with lane l^32, the running sum none
 //   O^T [D x rows]   += V_tile^T [D x keys] * P^T     (P straight from registers)
 // The cache keeps V transposed per block ([D][16 keys]), so V^T tiles are
-// staged with plain 16-byte copies.  K and V^T tiles are double buffered in
-// LDS (XOR-swizzled 16-byte chunks) and moved by the gfx950 LDS DMA
-// (global_load_lds_dwordx4), so the next tile streams in during the MFMAs
-// without passing through registers.
+// staged with plain 16-byte copies.  K and V^T tiles go through a 4-slot LDS
+// ring (XOR-swizzled 16-byte chunks), moved by the gfx950 LDS DMA
+// (global_load_lds_dwordx4) three tiles ahead of the MFMAs, without passing
+// through registers.  With one tile of look-ahead the DMA latency (K/V come
+// from L2 or the last-level cache, at a few KB per block) stalled the loop:
+// the DMAs took about 40% of the kernel's time on top of the math.
 #include <math.h>
 
 #include "common.h"
@@ -50,6 +52,8 @@ struct ACfg {
   static constexpr int KSLOTS = KT * CPRK, VSLOTS = D * VROW;
   static constexpr int LK = KSLOTS / NT;                 // K chunks moved per thread
   static constexpr int LV = VSLOTS / NT;                 // V^T chunks moved per thread
+  static constexpr int PER = LK + LV;                    // DMAs per thread per tile
+  static constexpr int NST = 4;                          // LDS ring slots (tiles)
   static_assert(LK >= 1 && LV >= 1, "tile too small for the workgroup");
   static_assert(NT == 512, "the kernel's launch bounds assume 512 threads");
 };
@@ -69,12 +73,12 @@ DEVI int v_swz(int d) { return (d >> 1) & 7; }
 constexpr float kRescaleLog2 = 8.f;
 
 template <typename T, int D>
-__global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__ q, T* __restrict__ attn,
+__global__ __launch_bounds__(512) void attn_prefill_f32_kernel(const T* __restrict__ q, T* __restrict__ attn,
                                                            int H, CacheView cache, BatchView batch) {
   using C = ACfg<T, D>;
   using vec = typename Chunk<T>::vec;
-  __shared__ u32x4 sK[2][C::KSLOTS];
-  __shared__ u32x4 sV[2][C::VSLOTS];
+  __shared__ u32x4 sK[C::NST][C::KSLOTS];
+  __shared__ u32x4 sV[C::NST][C::VSLOTS];
 
   const int G = cache.G;
   const int R = H / G;
@@ -102,7 +106,10 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
 
   const T* kpool = reinterpret_cast<const T*>(cache.k_pool);
   const T* vpool = reinterpret_cast<const T*>(cache.v_pool);
-  const int32_t* btab = cache.block_table + (size_t)seq * cache.max_blocks;
+  // block-table reads are wave-uniform: through the constant address space
+  // they become scalar loads, so the vector-memory counter counts DMAs only
+  const __attribute__((address_space(4))) int32_t* btab =
+      (const __attribute__((address_space(4))) int32_t*)(cache.block_table + (size_t)seq * cache.max_blocks);
 
   // this lane's query rows (one per 32-row block)
   int qpos[C::RB];
@@ -145,6 +152,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
   typedef int32_t i32x4v __attribute__((ext_vector_type(4)));
   auto fetch_blocks = [&](int kt) {
     const int last = cache.max_blocks - 1;
+    kt = __builtin_amdgcn_readfirstlane(kt);
     return i32x4v{btab[min(kt * 4 + 0, last)], btab[min(kt * 4 + 1, last)], btab[min(kt * 4 + 2, last)],
                   btab[min(kt * 4 + 3, last)]};
   };
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
       const int c = (slot % C::CPRK) ^ k_swz<C::CPRK>(key);
       const int kp = min(kt * C::KT + key, last);
       const size_t bk = (size_t)pick(blk, (kp - kt * C::KT) >> 4);
-      lds_dma16(kpool + ((bk * G + g) * 16 + (kp & 15)) * D + c * C::CH, &sK[st][base]);
+      glb_dma16_to(kpool + ((bk * G + g) * 16 + (kp & 15)) * D + c * C::CH, lds_address(&sK[st][base]));
     }
 #pragma unroll
     for (int i = 0; i < C::LV; ++i) {
@@ -178,7 +186,7 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
       const int c = (slot % C::VROW) ^ v_swz<C::VROW>(d);
       const int kp = min(kt * C::KT + c * C::CH, last & ~(C::CH - 1));  // first key of this chunk
       const size_t bk = (size_t)pick(blk, (kp - kt * C::KT) >> 4);
-      lds_dma16(vpool + ((bk * G + g) * D + d) * 16 + (kp & 15), &sV[st][base]);
+      glb_dma16_to(vpool + ((bk * G + g) * D + d) * 16 + (kp & 15), lds_address(&sV[st][base]));
     }
   };
   // After the DMA has landed: zero the values of keys past the end (a chunk
@@ -202,7 +210,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
     }
   };
 
-  const float scale = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(D)
+  // q arrives multiplied by log2(e)/sqrt(D) (QKV epilogue): scores are in exp2 units
+  constexpr float scale = 1.f;
   float m_run[C::RB], l_run[C::RB];
   f32x16 o[C::RB][C::NDB];
 #pragma unroll
@@ -215,19 +224,33 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
       for (int i = 0; i < 16; ++i) o[x][db][i] = 0.f;
   }
 
+  // Ring: tile kt sits in slot kt % NST.  Tiles kt+1 .. kt+NST-1 are in
+  // flight while tile kt computes; each thread waits for its own DMAs of a
+  // tile (vmcnt: the DMAs of the tiles issued after it may stay outstanding)
+  // and the barrier that ends an iteration publishes the tile to every wave
+  // and frees the slot of the tile just computed.
+  auto wait_tile = [&](int kt) {  // tile kt landed, for this thread's DMAs
+    const int after = min(ntiles - 1, kt + C::NST - 2) - kt;  // tiles issued after kt
+    if (after >= 2) wait_vmcnt<2 * C::PER>();
+    else if (after == 1) wait_vmcnt<C::PER>();
+    else wait_vmcnt<0>();
+  };
   i32x4v blk_next = fetch_blocks(0);
-  issue(0, 0, blk_next);
-  blk_next = fetch_blocks(1);
-  wait_all_loads();
+#pragma unroll
+  for (int t = 0; t < C::NST - 1; ++t) {
+    if (t < ntiles) issue(t, t, blk_next);
+    blk_next = fetch_blocks(t + 1);
+  }
+  wait_tile(0);
   finish(0, 0);
   __syncthreads();
 
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int st = kt & 1;
+    const int st = kt % C::NST;
     const int k0 = kt * C::KT;
-    if (kt + 1 < ntiles) {
-      issue(kt + 1, st ^ 1, blk_next);  // lands while this tile computes
-      blk_next = fetch_blocks(kt + 2);
+    if (kt + C::NST - 1 < ntiles) {  // into the slot of tile kt-1 (freed by the last barrier)
+      issue(kt + C::NST - 1, (kt + C::NST - 1) % C::NST, blk_next);
+      blk_next = fetch_blocks(kt + C::NST);
     }
     // the 64-key tile is consumed in two 32-key halves (fewer live registers)
 #pragma unroll
@@ -345,8 +368,8 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
           }
     }
     if (kt + 1 < ntiles) {
-      wait_all_loads();
-      finish(kt + 1, st ^ 1);
+      wait_tile(kt + 1);
+      finish(kt + 1, (kt + 1) % C::NST);
     }
     __syncthreads();
   }
@@ -377,12 +400,302 @@ __global__ __launch_bounds__(512) void attn_prefill_kernel(const T* __restrict__
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// bf16 kernel.  Same work split and MFMA formulation as above; the loop is
+// built to keep per-tile VALU work to the softmax itself:
+//  * K/V tiles move through a 4-slot LDS ring by buffer LDS DMA, three tiles
+//    ahead.  One DMA instruction never spans two 16-key cache blocks, so its
+//    source is a per-block base held in SGPRs (from the block table, read by
+//    scalar loads) plus a per-lane offset computed once.  V^T is kept in LDS
+//    block by block ([4][D][16 keys], a copy of the cache layout, whose key
+//    order vperm_pos makes each 16-byte half of a row one lane group's MFMA
+//    operand) with the two halves swapped on rows 8..15 of every 16, which
+//    keeps the fragment reads free of bank conflicts.
+//  * LDS fragment addresses are per-lane bases computed once plus the slot
+//    offset.
+//  * q arrives scaled by log2(e)/sqrt(D), and the QK product starts from an
+//    accumulator holding -m (the row's running max), so the MFMA result is
+//    already s - m in exp2 units: p = exp2(acc) with no VALU step between.
+// ---------------------------------------------------------------------------
+template <int D>
+struct BCfg {
+  static constexpr int KT = 64;                 // keys per tile: four 16-key cache blocks
+  static constexpr int NW = 8, NT = 64 * NW;    // waves (2 per SIMD), threads
+  static constexpr int ROWS = NW * 32;          // query rows per workgroup
+  static constexpr int NST = 4;                 // LDS ring slots (tiles)
+  static constexpr int CPRK = D / 8;            // 16-byte chunks per K row
+  static constexpr int NQ = D / 16;             // QK k-steps
+  static constexpr int NDB = D / 32;            // 32-row blocks of O^T
+  static constexpr int PIECE = 16 * D * 2;      // bytes of one block's K (or V^T) for one KV group
+  static constexpr int TILE = 4 * PIECE;        // bytes of a K (or V^T) tile
+  static constexpr int SLOT = 2 * TILE;         // K tile, then V^T tile
+  static constexpr int LK = TILE / 1024 / NW;   // K DMAs per thread per tile (= V DMAs)
+  static constexpr int PER = 2 * LK;            // DMAs per thread per tile
+  static_assert(LK >= 1 && PIECE % 1024 == 0, "one DMA instruction per 1 KB, inside one block");
+  static_assert(NST * SLOT <= 160 * 1024, "LDS");
+};
+
+template <int D>
+__global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __restrict__ q, bf16* __restrict__ attn,
+                                                                int H, CacheView cache, BatchView batch) {
+  using C = BCfg<D>;
+  __shared__ u32x4 ring[C::NST * C::SLOT / 16];
+
+  const int G = cache.G;
+  const int R = H / G;
+  const int P = C::ROWS / R;  // positions per workgroup
+  const int S = batch.seq_len;
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const int nrb = (S + P - 1) / P;
+  const int rb = nrb - 1 - (int)blockIdx.y;
+  const int seq = batch.desc[2 * b];
+  const int start = batch.desc[2 * b + 1];
+  const int kv_len = start + S;
+  const int HD = H * D;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, l32 = lane & 31;
+
+  // query row j of the workgroup -> (head, sequence index); rows past the end
+  // mirror the block's first row (computed, never stored)
+  const int j = wave * 32 + l32;
+  const int head = g * R + j / P;
+  const bool active = rb * P + j % P < S;
+  const int sidx = active ? rb * P + j % P : rb * P;
+  const int qpos = start + sidx;
+  int wmax = qpos, wmin = qpos;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    wmax = max(wmax, __shfl_xor(wmax, m, 64));
+    wmin = min(wmin, __shfl_xor(wmin, m, 64));
+  }
+  wmax = __builtin_amdgcn_readfirstlane(wmax);
+  wmin = __builtin_amdgcn_readfirstlane(wmin);
+  const int last_s = min(S, (rb + 1) * P) - 1;
+  const int ntiles = (start + last_s) / C::KT + 1;
+
+  // Q fragments (B operand of S^T), resident for the whole key loop
+  bf16x8 qf[C::NQ];
+  {
+    const bf16* qp = q + ((size_t)b * S + sidx) * HD + (size_t)head * D;
+#pragma unroll
+    for (int kk = 0; kk < C::NQ; ++kk) qf[kk] = load_chunk<bf16>(qp + (2 * kk + hl) * 8);
+  }
+
+  // ---- DMA plan (per thread, fixed for all tiles) ----
+  // K DMA i: 16-byte LDS slot (wave * LK + i) * 64 + lane of the K tile =
+  // row `key`, physical chunk p holding logical chunk p ^ (key & (CPRK-1));
+  // V DMA i: byte (wave * LK + i) * 1024 + 16 * lane of the V^T tile.
+  int koff[C::LK], voff[C::LK], kblk[C::LK], vblk[C::LK], vchk[C::LK];
+#pragma unroll
+  for (int i = 0; i < C::LK; ++i) {
+    const int qd = wave * C::LK + i;
+    const int slot = qd * 64 + lane;
+    const int key = slot / C::CPRK, p = slot % C::CPRK;
+    const int c = p ^ (key & (C::CPRK - 1));
+    kblk[i] = __builtin_amdgcn_readfirstlane((qd * 64 / C::CPRK) >> 4);
+    koff[i] = (key & 15) * D * 2 + c * 16;
+    const int byte = qd * 1024 + lane * 16;
+    vblk[i] = __builtin_amdgcn_readfirstlane(qd * 1024 / C::PIECE);
+    const int o = byte % C::PIECE, d = o >> 5, vp = (o >> 4) & 1, vc = vp ^ ((d >> 3) & 1);
+    voff[i] = d * 32 + vc * 16;
+    vchk[i] = vc;  // row half: keys 4vc..4vc+3 and 8+4vc..8+4vc+3 of block vblk
+  }
+  const char* kpool = reinterpret_cast<const char*>(cache.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(cache.v_pool);
+  // block-table reads are wave-uniform: through the constant address space
+  // they become scalar loads, so the vector-memory counter counts DMAs only
+  const __attribute__((address_space(4))) int32_t* btab =
+      (const __attribute__((address_space(4))) int32_t*)(cache.block_table + (size_t)seq * cache.max_blocks);
+  const uint32_t ring_lds = lds_address(ring);
+  // blocks of tile kt past the sequence's last block are replaced by the last
+  // one (their keys are masked and their values zeroed)
+  auto issue = [&](int kt, int st) {
+    const int ulast = min(3, ((kv_len - 1) >> 4) - kt * 4);
+    int32_t blk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) blk[u] = btab[kt * 4 + min(u, ulast)];
+    const uint32_t base = ring_lds + (uint32_t)(st * C::SLOT);
+#pragma unroll
+    for (int i = 0; i < C::LK; ++i) {
+      const int u = kblk[i];
+      const int32_t bk = u == 0 ? blk[0] : u == 1 ? blk[1] : u == 2 ? blk[2] : blk[3];
+      const i32x4 rs = make_rsrc(kpool + ((size_t)bk * G + g) * C::PIECE, C::PIECE);
+      buf_dma16_to(rs, base + (uint32_t)((wave * C::LK + i) * 1024), koff[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < C::LK; ++i) {
+      const int u = vblk[i];
+      const int32_t bk = u == 0 ? blk[0] : u == 1 ? blk[1] : u == 2 ? blk[2] : blk[3];
+      const i32x4 rs = make_rsrc(vpool + ((size_t)bk * G + g) * C::PIECE, C::PIECE);
+      buf_dma16_to(rs, base + (uint32_t)(C::TILE + (wave * C::LK + i) * 1024), voff[i]);
+    }
+  };
+  // After the DMA has landed: zero the values of keys past the end (only the
+  // last tile has any); each thread fixes the chunks its own DMAs wrote.
+  auto finish = [&](int kt, int st) {
+    if ((kt + 1) * C::KT <= kv_len) return;
+    u32x4* vt = ring + (st * C::SLOT + C::TILE) / 16;
+#pragma unroll
+    for (int i = 0; i < C::LK; ++i) {
+      const int k0 = kt * C::KT + 16 * vblk[i] + 4 * vchk[i];  // element e holds key k0 + e + 4 (e >= 4)
+      if (k0 + 12 > kv_len) {
+        const int idx = (wave * C::LK + i) * 64 + lane;
+        bf16x8 v = __builtin_bit_cast(bf16x8, vt[idx]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (k0 + e + (e & 4) >= kv_len) v[e] = from_f32<bf16>(0.f);
+        vt[idx] = __builtin_bit_cast(u32x4, v);
+      }
+    }
+  };
+  auto wait_tile = [&](int kt) {  // tile kt landed, for this thread's DMAs
+    const int after = min(ntiles - 1, kt + C::NST - 2) - kt;  // tiles issued after kt
+    if (after >= 2) wait_vmcnt<2 * C::PER>();
+    else if (after == 1) wait_vmcnt<C::PER>();
+    else wait_vmcnt<0>();
+  };
+
+  // ---- fragment addresses (bytes from the slot base) ----
+  // K (A operand of S^T): key l32 of the half, chunk 2kk + hl
+  int kaddr[C::NQ];
+#pragma unroll
+  for (int kk = 0; kk < C::NQ; ++kk)
+    kaddr[kk] = l32 * C::CPRK * 16 + (((2 * kk + hl) ^ (l32 & (C::CPRK - 1))) * 16);
+  // V^T (A operand of O^T): row d = 32 db + l32 of block 2kb + m; lane group
+  // hl takes row half hl (keys 4hl..4hl+3 and 8+4hl..8+4hl+3, the keys its
+  // P registers hold)
+  const int vaddr = C::TILE + l32 * 32 + ((hl ^ ((l32 >> 3) & 1)) * 16);
+
+  float m_run = 0.f, l_run = 0.f;  // m_run: running max in exp2 units (valid once `first` is false)
+  bool first = true;
+  f32x16 negm, o[C::NDB];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negm[i] = 0.f;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[db][i] = 0.f;
+
+  // Ring: tile kt sits in slot kt % NST; tiles kt+1 .. kt+NST-1 are in flight
+  // while tile kt computes.  The barrier ending an iteration publishes tile
+  // kt+1 to every wave and frees the slot of tile kt.
+#pragma unroll
+  for (int t = 0; t < C::NST - 1; ++t)
+    if (t < ntiles) issue(t, t);
+  wait_tile(0);
+  finish(0, 0);
+  __syncthreads();
+
+  const char* lds = reinterpret_cast<const char*>(ring);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int st = kt % C::NST;
+    const int k0 = kt * C::KT;
+    if (kt + C::NST - 1 < ntiles) issue(kt + C::NST - 1, (kt + C::NST - 1) % C::NST);
+    const char* sb = lds + st * C::SLOT;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int kh = k0 + 32 * kb;
+      if (kh > wmax) continue;  // every row of this wave is before these keys
+      // ---- S^T - m = K Q^T + (-m) ----
+      bf16x8 ka[C::NQ];
+#pragma unroll
+      for (int kk = 0; kk < C::NQ; ++kk)
+        ka[kk] = *reinterpret_cast<const bf16x8*>(sb + kaddr[kk] + kb * 32 * C::CPRK * 16);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 sc = mfma32_chunk(negm, ka[0], qf[0]);
+#pragma unroll
+      for (int kk = 1; kk < C::NQ; ++kk) sc = mfma32_chunk(sc, ka[kk], qf[kk]);
+      // V^T fragments of the half: their latency hides behind the softmax
+      bf16x8 va[2][C::NDB];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          va[m][db] = *reinterpret_cast<const bf16x8*>(sb + vaddr + (2 * kb + m) * C::PIECE + db * 32 * 32);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- online softmax: lane = one query row, 16 of the half's 32 keys ----
+      if (kh + 31 > wmin) {  // the half reaches the diagonal of some row of this wave
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kp = kh + 8 * (i >> 2) + 4 * hl + (i & 3);
+          if (kp > qpos) sc[i] = -INFINITY;
+        }
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // max of s - m over the 32 keys
+      // the running max is raised lazily: only when a score exceeds it by
+      // more than 2^8, so unnormalised P stays <= 256; the final division
+      // uses the same stale max, so the result is exact
+      const bool grow = first || mx > kRescaleLog2;
+      if (wave_any(grow)) {
+        const float shift = grow ? mx : 0.f;
+        const float alpha = first ? 0.f : fast_exp2(-shift);
+        m_run = first ? mx : m_run + shift;
+        first = false;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sc[i] -= shift;
+          negm[i] = -m_run;
+        }
+      }
+      bf16x8 pv[2];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(sc[i]);
+        psum += p;
+        pv[i >> 3][i & 7] = from_f32<bf16>(p);
+      }
+      l_run += psum;
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) o[db] = mfma32_chunk(o[db], va[m][db], pv[m]);
+    }
+    if (kt + 1 < ntiles) {
+      wait_tile(kt + 1);
+      finish(kt + 1, (kt + 1) % C::NST);
+    }
+    __syncthreads();
+  }
+
+  if (!active) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = 1.f / l_tot;
+  const int tok = b * S + sidx, col0 = head * D;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+    for (int ig = 0; ig < 4; ++ig) {
+      const int d0 = 32 * db + 8 * ig + 4 * hl;
+      // the o_proj GEMM's operand: tiled bf16
+      *reinterpret_cast<bf16x4*>(attn + tiled_off(tok, col0 + d0, HD)) =
+          bf16x4{from_f32<bf16>(o[db][4 * ig] * inv), from_f32<bf16>(o[db][4 * ig + 1] * inv),
+                 from_f32<bf16>(o[db][4 * ig + 2] * inv), from_f32<bf16>(o[db][4 * ig + 3] * inv)};
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_d(const void* q, void* attn, int H, const CacheView& c, const BatchView& b, hipStream_t s) {
   const int R = H / c.G;
   const int P = ACfg<T, D>::ROWS / R;
   dim3 grid(c.G * b.batch, (b.seq_len + P - 1) / P);
-  attn_prefill_kernel<T, D><<<grid, ACfg<T, D>::NT, 0, s>>>(reinterpret_cast<const T*>(q), reinterpret_cast<T*>(attn), H, c, b);
+  if constexpr (sizeof(T) == 2)
+    attn_prefill_bf16_kernel<D><<<grid, BCfg<D>::NT, 0, s>>>(reinterpret_cast<const bf16*>(q),
+                                                             reinterpret_cast<bf16*>(attn), H, c, b);
+  else
+    attn_prefill_f32_kernel<T, D><<<grid, ACfg<T, D>::NT, 0, s>>>(reinterpret_cast<const T*>(q),
+                                                                  reinterpret_cast<T*>(attn), H, c, b);
   return hipGetLastError();
 }
 

@@ -154,6 +154,12 @@ __device__ __forceinline__ void buf_dma16_to(i32x4 rsrc, uint32_t lds, int voffs
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
 }
+// LDS DMA from a flat global address (lane i's 16 bytes at g land at lds + 16 i),
+// hidden from the compiler in the same way: the caller orders LDS with
+// wait_vmcnt and barriers.
+__device__ __forceinline__ void glb_dma16_to(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(g) : "memory", "m0");
+}
 __device__ __forceinline__ void buf_dma16_async(i32x4 rsrc, const void* lds_base, int voffset) {
   buf_dma16_to(rsrc, lds_address(lds_base), voffset);
 }
@@ -173,6 +179,12 @@ template <typename T> DEVI T ceil_div(T a, T b) { return (a + b - 1) / b; }
 // row count rounded up to 256.  Returns the element offset of (r, k).
 // ---------------------------------------------------------------------------
 constexpr int kTileRows = 256, kTileCols = 32, kTileElems = kTileRows * kTileCols;
+
+// bf16 V cache blocks hold V^T ([D][16 keys]) with the keys of a row in the
+// order 0-3, 8-11, 4-7, 12-15: each 16-byte half of a row then holds exactly
+// the eight keys one lane group feeds to a 32x32x16 MFMA (keys 4h..4h+3 and
+// 8+4h..8+4h+3 for lane group h).  Position of key k (0..15) in the row:
+DEVI int vperm_pos(int k) { return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
 DEVI size_t tiled_off(int r, int k, int K) {
   return ((size_t)(r >> 8) * (size_t)(K >> 5) + (size_t)(k >> 5)) * kTileElems + (size_t)((r & 255) * 32 + (k & 31));
 }

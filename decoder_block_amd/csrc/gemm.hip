@@ -105,6 +105,9 @@ DEVI void epilogue(const GemmArgs& a, int t, int f, f32x4 v) {
       v[3] = e1 * s1 + o1 * c1;
     }
     if (f < HD) {
+      // q is stored pre-multiplied by log2(e)/sqrt(D), so the attention kernels'
+      // scores come out in exp2 units (scaled in fp32, then rounded once)
+      v *= 1.4426950408889634f * __frsqrt_rn((float)D);
       store4(reinterpret_cast<T*>(a.q_out) + (size_t)t * HD + f, v[0], v[1], v[2], v[3]);
     } else {
       const bool is_k = f < HD + KD;
@@ -114,8 +117,9 @@ DEVI void epilogue(const GemmArgs& a, int t, int f, f32x4 v) {
       if (is_k) {  // K block [16 slots][D]
         T* dst = reinterpret_cast<T*>(a.cache.k_pool) + ((blk * G + g) * 16 + (pos & 15)) * D + dd;
         store4(dst, v[0], v[1], v[2], v[3]);
-      } else {     // V block kept transposed: [D][16 slots]
-        T* dst = reinterpret_cast<T*>(a.cache.v_pool) + ((blk * G + g) * D + dd) * 16 + (pos & 15);
+      } else {     // V block kept transposed: [D][16 slots] (bf16: keys in vperm_pos order)
+        const int slot = sizeof(T) == 2 ? vperm_pos(pos & 15) : (pos & 15);
+        T* dst = reinterpret_cast<T*>(a.cache.v_pool) + ((blk * G + g) * D + dd) * 16 + slot;
         dst[0] = from_f32<T>(v[0]);
         dst[16] = from_f32<T>(v[1]);
         dst[32] = from_f32<T>(v[2]);
@@ -473,6 +477,103 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
     static_assert(NS == 4, "ring of four slots");
   }
   wait_vmcnt<0>();
+
+  if constexpr (EPI == (int)Epi::SWIGLU) {
+    // The tile's s = SiLU(r g) * (r u) is 256 tokens x 128 columns, i.e. the
+    // four 16 KB tiles (one row block, four column blocks) of the down GEMM's
+    // operand.  It is assembled in LDS (the ring is free now) and written out
+    // as contiguous 16-byte stores, instead of 4-byte pieces scattered over
+    // 32 rows per store instruction.
+    constexpr int RS = 40;  // LDS row pitch in elements: 80 bytes keeps 16-byte alignment, 2-way write conflicts
+    bf16* st = reinterpret_cast<bf16*>(ring);
+    __syncthreads();  // every wave is done with the ring
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tl = wm * 128 + 32 * j + l32;
+      const float r = m0 + tl < a.M ? a.rowscale[m0 + tl] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int cl = wn * 64 + 16 * i + 4 * g + 2 * lh;  // s column inside the tile (even)
+          const float v0 = acc[i][j][4 * g] * r, v1 = acc[i][j][4 * g + 1] * r;
+          const float v2 = acc[i][j][4 * g + 2] * r, v3 = acc[i][j][4 * g + 3] * r;
+          *reinterpret_cast<bf16x2*>(st + ((cl >> 5) * 256 + tl) * RS + (cl & 31)) =
+              bf16x2{from_f32<bf16>(silu(v0) * v1), from_f32<bf16>(silu(v2) * v3)};
+        }
+    }
+    __syncthreads();
+    bf16* ob = reinterpret_cast<bf16*>(a.out) + tiled_off(m0, n0 / 2, a.ldo);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int idx = p * 256 + tid;  // 16-byte piece: column block, row, chunk
+      const int cb = idx >> 10, row = (idx >> 2) & 255, ch = idx & 3;
+      if (m0 + row < a.M)
+        *reinterpret_cast<u32x4*>(ob + cb * kTileElems + row * 32 + ch * 8) =
+            *reinterpret_cast<const u32x4*>(st + (cb * 256 + row) * RS + ch * 8);
+    }
+    return;
+  }
+
+  if constexpr (EPI == (int)Epi::RESID_H || EPI == (int)Epi::RESID_OUT) {
+    // Residual epilogues: each token row of the tile is 256 contiguous
+    // features of a row-major [M][N] output.  The accumulators go through LDS
+    // one half of the tile (128 tokens, fp32, 128 KB) at a time, so that the
+    // residual loads and the output stores cover whole rows: a wave moves one
+    // token's 1 KB (fp32) per instruction.  16-byte chunk c of LDS row r sits
+    // at chunk c ^ (r & 63), which keeps both the per-lane writes (32 rows,
+    // one chunk) and the row reads free of bank conflicts.
+    f32x4* st = reinterpret_cast<f32x4*>(ring);
+    __syncthreads();  // every wave is done with the ring
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      // the half's residual rows are loaded first, so that their latency
+      // overlaps the LDS writes and the barrier
+      f32x4 res[32];
+#pragma unroll
+      for (int p = 0; p < 32; ++p) {
+        const int t = m0 + hh * 128 + p * 4 + wave;
+        const size_t o = (size_t)min(t, a.M - 1) * a.ldo + n0 + 4 * lane;
+        if constexpr (EPI == (int)Epi::RESID_H)
+          res[p] = load4(reinterpret_cast<const T*>(a.resid) + o);
+        else
+          res[p] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.resid) + o);
+      }
+      if (wm == hh) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int r = 32 * j + l32, c = (wn * 128 + 32 * i + 8 * g + 4 * lh) >> 2;
+              st[r * 64 + (c ^ (r & 63))] =
+                  f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+            }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < 32; ++p) {
+        const int r = p * 4 + wave, c = lane;  // wave-uniform row, lane = 16-byte chunk
+        const int t = m0 + hh * 128 + r;
+        if (t < a.M) {
+          const f32x4 v = st[r * 64 + (c ^ (r & 63))];
+          const size_t o = (size_t)t * a.ldo + n0 + 4 * c;
+          if constexpr (EPI == (int)Epi::RESID_H) {  // h = x + attn W_o^T, fp32
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = res[p] + v;
+          } else {  // out = h + s W_down^T
+            const f32x4 hv = res[p] + v;
+            if (a.out_dtype == DType::F32)
+              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = hv;
+            else
+              store4(reinterpret_cast<bf16*>(a.out) + o, hv[0], hv[1], hv[2], hv[3]);
+          }
+        }
+      }
+      __syncthreads();
+    }
+    return;
+  }
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)

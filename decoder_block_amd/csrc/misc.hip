@@ -42,7 +42,8 @@ __global__ __launch_bounds__(256) void upload_kernel(Upload u) {
   for (int i = threadIdx.x; i < u.n; i += 256) u.base[(u.idx[i] >> 31) & 1][u.idx[i] & 0x7fffffff] = u.val[i];
 }
 
-// K pool [blk][G][16][D]; V pool [blk][G][D][16] (V transposed per block).
+// K pool [blk][G][16][D]; V pool [blk][G][D][16] (V transposed per block;
+// bf16 rows hold the keys in vperm_pos order).
 template <typename T>
 __global__ __launch_bounds__(256) void kv_copy_kernel(CacheView c, int seq, int start, int n, T* __restrict__ k,
                                                       T* __restrict__ v, int to_cache) {
@@ -58,7 +59,7 @@ __global__ __launch_bounds__(256) void kv_copy_kernel(CacheView c, int seq, int 
     const int pos = start + t;
     const size_t blk = (size_t)bt[pos >> 4];
     const size_t ko = ((blk * G + g) * 16 + (pos & 15)) * D + d;
-    const size_t vo = ((blk * G + g) * D + d) * 16 + (pos & 15);
+    const size_t vo = ((blk * G + g) * D + d) * 16 + (sizeof(T) == 2 ? vperm_pos(pos & 15) : (pos & 15));
     if (to_cache) {
       kp[ko] = k[i];
       vp[vo] = v[i];
