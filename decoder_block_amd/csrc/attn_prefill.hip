@@ -483,25 +483,32 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
 #pragma unroll
     for (int kk = 0; kk < C::NQ; ++kk) qf[kk] = load_chunk<bf16>(qp + (2 * kk + hl) * 8);
   }
+  // The Q loads complete here, before the first DMA: the compiler does not
+  // see the DMAs (inline assembly), and a Q load it still believed pending
+  // would make it wait on the vector-memory counter inside the loop, which
+  // would drain the DMAs of the tiles in flight.
+  wait_vmcnt<0>();
 
   // ---- DMA plan (per thread, fixed for all tiles) ----
   // K DMA i: 16-byte LDS slot (wave * LK + i) * 64 + lane of the K tile =
   // row `key`, physical chunk p holding logical chunk p ^ (key & (CPRK-1));
   // V DMA i: byte (wave * LK + i) * 1024 + 16 * lane of the V^T tile.
-  int koff[C::LK], voff[C::LK], kblk[C::LK], vblk[C::LK], vchk[C::LK];
+  // Every DMA of a wave touches the same 16-key block of the tile, block
+  // wave / 2 (8 waves x PER KB cover the 4 blocks' K and V^T pieces in order).
+  static_assert(C::NW == 8 && C::PIECE == 2 * C::LK * 1024, "two waves per 16-key block");
+  const int my_u = wave >> 1;
+  int koff[C::LK], voff[C::LK], vchk[C::LK];
 #pragma unroll
   for (int i = 0; i < C::LK; ++i) {
     const int qd = wave * C::LK + i;
     const int slot = qd * 64 + lane;
     const int key = slot / C::CPRK, p = slot % C::CPRK;
     const int c = p ^ (key & (C::CPRK - 1));
-    kblk[i] = __builtin_amdgcn_readfirstlane((qd * 64 / C::CPRK) >> 4);
     koff[i] = (key & 15) * D * 2 + c * 16;
     const int byte = qd * 1024 + lane * 16;
-    vblk[i] = __builtin_amdgcn_readfirstlane(qd * 1024 / C::PIECE);
     const int o = byte % C::PIECE, d = o >> 5, vp = (o >> 4) & 1, vc = vp ^ ((d >> 3) & 1);
     voff[i] = d * 32 + vc * 16;
-    vchk[i] = vc;  // row half: keys 4vc..4vc+3 and 8+4vc..8+4vc+3 of block vblk
+    vchk[i] = vc;  // row half: keys 4vc..4vc+3 and 8+4vc..8+4vc+3 of block my_u
   }
   const char* kpool = reinterpret_cast<const char*>(cache.k_pool);
   const char* vpool = reinterpret_cast<const char*>(cache.v_pool);
@@ -510,28 +517,22 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
   const __attribute__((address_space(4))) int32_t* btab =
       (const __attribute__((address_space(4))) int32_t*)(cache.block_table + (size_t)seq * cache.max_blocks);
   const uint32_t ring_lds = lds_address(ring);
-  // blocks of tile kt past the sequence's last block are replaced by the last
-  // one (their keys are masked and their values zeroed)
-  auto issue = [&](int kt, int st) {
-    const int ulast = min(3, ((kv_len - 1) >> 4) - kt * 4);
-    int32_t blk[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) blk[u] = btab[kt * 4 + min(u, ulast)];
+  // The physical block this wave moves for tile kt; blocks past the
+  // sequence's last one are replaced by it (their keys are masked and their
+  // values zeroed).  Read one tile ahead of its use.
+  auto block_of = [&](int kt) {
+    const int ulast = ((kv_len - 1) >> 4) - kt * 4;
+    return btab[kt * 4 + min(my_u, ulast)];
+  };
+  auto issue = [&](int st, int32_t bk) {
     const uint32_t base = ring_lds + (uint32_t)(st * C::SLOT);
+    const size_t piece = ((size_t)bk * G + g) * C::PIECE;
+    const i32x4 rk = make_rsrc(kpool + piece, C::PIECE), rv = make_rsrc(vpool + piece, C::PIECE);
 #pragma unroll
-    for (int i = 0; i < C::LK; ++i) {
-      const int u = kblk[i];
-      const int32_t bk = u == 0 ? blk[0] : u == 1 ? blk[1] : u == 2 ? blk[2] : blk[3];
-      const i32x4 rs = make_rsrc(kpool + ((size_t)bk * G + g) * C::PIECE, C::PIECE);
-      buf_dma16_to(rs, base + (uint32_t)((wave * C::LK + i) * 1024), koff[i]);
-    }
+    for (int i = 0; i < C::LK; ++i) buf_dma16_to(rk, base + (uint32_t)((wave * C::LK + i) * 1024), koff[i]);
 #pragma unroll
-    for (int i = 0; i < C::LK; ++i) {
-      const int u = vblk[i];
-      const int32_t bk = u == 0 ? blk[0] : u == 1 ? blk[1] : u == 2 ? blk[2] : blk[3];
-      const i32x4 rs = make_rsrc(vpool + ((size_t)bk * G + g) * C::PIECE, C::PIECE);
-      buf_dma16_to(rs, base + (uint32_t)(C::TILE + (wave * C::LK + i) * 1024), voff[i]);
-    }
+    for (int i = 0; i < C::LK; ++i)
+      buf_dma16_to(rv, base + (uint32_t)(C::TILE + (wave * C::LK + i) * 1024), voff[i]);
   };
   // After the DMA has landed: zero the values of keys past the end (only the
   // last tile has any); each thread fixes the chunks its own DMAs wrote.
@@ -540,7 +541,7 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
     u32x4* vt = ring + (st * C::SLOT + C::TILE) / 16;
 #pragma unroll
     for (int i = 0; i < C::LK; ++i) {
-      const int k0 = kt * C::KT + 16 * vblk[i] + 4 * vchk[i];  // element e holds key k0 + e + 4 (e >= 4)
+      const int k0 = kt * C::KT + 16 * my_u + 4 * vchk[i];  // element e holds key k0 + e + 4 (e >= 4)
       if (k0 + 12 > kv_len) {
         const int idx = (wave * C::LK + i) * 64 + lane;
         bf16x8 v = __builtin_bit_cast(bf16x8, vt[idx]);
@@ -584,7 +585,8 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
   // kt+1 to every wave and frees the slot of tile kt.
 #pragma unroll
   for (int t = 0; t < C::NST - 1; ++t)
-    if (t < ntiles) issue(t, t);
+    if (t < ntiles) issue(t, block_of(t));
+  int32_t bk_next = block_of(min(C::NST - 1, ntiles - 1));
   wait_tile(0);
   finish(0, 0);
   __syncthreads();
@@ -593,7 +595,10 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
   for (int kt = 0; kt < ntiles; ++kt) {
     const int st = kt % C::NST;
     const int k0 = kt * C::KT;
-    if (kt + C::NST - 1 < ntiles) issue(kt + C::NST - 1, (kt + C::NST - 1) % C::NST);
+    if (kt + C::NST - 1 < ntiles) {
+      issue((kt + C::NST - 1) % C::NST, bk_next);
+      bk_next = block_of(min(kt + C::NST, ntiles - 1));
+    }
     const char* sb = lds + st * C::SLOT;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
