@@ -91,6 +91,28 @@ DEVI f32x4 rope4(f32x4 v, const GemmArgs& a, int pos, int dd) {
 }
 DEVI float q_scale(int D) { return 1.4426950408889634f * __frsqrt_rn((float)D); }
 
+// Rotated q or k values of features dd..dd+3 of one head, to the head's first
+// element `head`.  Interleaved RoPE: in place.  Half-split RoPE: the packed
+// rows of the head were reordered so that pair i = (i, i + D/2) sits in rows
+// 2i, 2i+1; (v0, v2) go back to positions dd/2, dd/2 + 1 and (v1, v3) to
+// dd/2 + D/2, dd/2 + D/2 + 1.
+template <typename T>
+DEVI void store_head4(T* head, int dd, f32x4 v, int half_split, int D) {
+  if (!half_split) {
+    store4(head + dd, v[0], v[1], v[2], v[3]);
+    return;
+  }
+  T* lo = head + dd / 2;
+  T* hi = lo + D / 2;
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x2*>(lo) = f32x2{v[0], v[2]};
+    *reinterpret_cast<f32x2*>(hi) = f32x2{v[1], v[3]};
+  } else {
+    *reinterpret_cast<bf16x2*>(lo) = bf16x2{from_f32<bf16>(v[0]), from_f32<bf16>(v[2])};
+    *reinterpret_cast<bf16x2*>(hi) = bf16x2{from_f32<bf16>(v[1]), from_f32<bf16>(v[3])};
+  }
+}
+
 // Epilogue for one lane-quad: token t, features f .. f+3, accumulator v.
 template <typename T, int EPI>
 DEVI void epilogue(const GemmArgs& a, int t, int f, f32x4 v) {
@@ -112,15 +134,16 @@ DEVI void epilogue(const GemmArgs& a, int t, int f, f32x4 v) {
       // q is stored pre-multiplied by log2(e)/sqrt(D), so the attention kernels'
       // scores come out in exp2 units (scaled in fp32, then rounded once)
       v *= q_scale(D);
-      store4(reinterpret_cast<T*>(a.q_out) + (size_t)t * HD + f, v[0], v[1], v[2], v[3]);
+      const int dd = f % D;
+      store_head4(reinterpret_cast<T*>(a.q_out) + (size_t)t * HD + (f - dd), dd, v, a.rope_half, D);
     } else {
       const bool is_k = f < HD + KD;
       const int kf = is_k ? f - HD : f - HD - KD;
       const int g = kf / D, dd = kf - g * D;
       const size_t blk = (size_t)a.cache.block_table[(size_t)seq * a.cache.max_blocks + (pos >> 4)];
       if (is_k) {  // K block [16 slots][D]
-        T* dst = reinterpret_cast<T*>(a.cache.k_pool) + ((blk * G + g) * 16 + (pos & 15)) * D + dd;
-        store4(dst, v[0], v[1], v[2], v[3]);
+        T* row = reinterpret_cast<T*>(a.cache.k_pool) + ((blk * G + g) * 16 + (pos & 15)) * D;
+        store_head4(row, dd, v, a.rope_half, D);
       } else {     // V block kept transposed: [D][16 slots] (bf16: keys in vperm_pos order)
         const int slot = sizeof(T) == 2 ? vperm_pos(pos & 15) : (pos & 15);
         T* dst = reinterpret_cast<T*>(a.cache.v_pool) + ((blk * G + g) * D + dd) * 16 + slot;
@@ -579,11 +602,11 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
           v = rope4(v, a, pos, dd);
           if (f < HD) {
             v *= qs;
-            store4(reinterpret_cast<bf16*>(a.q_out) + (size_t)t * HD + f, v[0], v[1], v[2], v[3]);
+            store_head4(reinterpret_cast<bf16*>(a.q_out) + (size_t)t * HD + (f - dd), dd, v, a.rope_half, D);
           } else {
             const size_t blk = (size_t)__builtin_amdgcn_readlane(blk_l, p);
-            store4(reinterpret_cast<bf16*>(a.cache.k_pool) + ((blk * G + g) * 16 + (pos & 15)) * D + dd, v[0], v[1],
-                   v[2], v[3]);
+            store_head4(reinterpret_cast<bf16*>(a.cache.k_pool) + ((blk * G + g) * 16 + (pos & 15)) * D, dd, v,
+                        a.rope_half, D);
           }
         }
       }

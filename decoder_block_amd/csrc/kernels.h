@@ -47,6 +47,7 @@ struct GemmArgs {
   BatchView batch;
   const float* rope_cos;  // [max_position][D/2]
   const float* rope_sin;
+  int rope_half;  // 1: the packed q/k rows of a head are ordered 0, D/2, 1, D/2+1, ... (half-split RoPE)
   int H;
   // residual / output epilogues
   const void* resid;  // RESID_H: x [M][N] (layer dtype); RESID_OUT: h [M][N] fp32
@@ -99,9 +100,11 @@ hipError_t launch_attn_decode_combine(DType t, const float* partial, void* attn,
 // Weight packing.  dst[r][c] = src[r][c] * (gamma ? gamma[c] : 1) for r < rows,
 // c < cols, with ldd columns (bf16: tiled, fp32: row-major); the caller zeroes
 // the buffer first, so padded rows and columns stay zero.  Row r of the source
-// lands at dst row (r * row_mul + row_add).
+// lands at dst row (r' * row_mul + row_add), where r' = r, or with head_pairs
+// = D > 0 the rows of each D-row head reordered so that rows w and w + D/2
+// become adjacent: w < D/2 -> 2w, w >= D/2 -> 2(w - D/2) + 1.
 hipError_t launch_pack(DType t, const void* src, const void* gamma, void* dst, int rows,
-                       int cols, int ldd, int row_mul, int row_add, hipStream_t s);
+                       int cols, int ldd, int row_mul, int row_add, int head_pairs, hipStream_t s);
 hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s);
 // dst[i] = float(src[i]) for n elements of the layer dtype.
 hipError_t launch_to_f32(DType t, const void* src, float* dst, int n, hipStream_t s);

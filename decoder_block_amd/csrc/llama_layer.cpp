@@ -37,6 +37,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 struct Shape {
   int d, I, I_pad, H, G, D, HD, KD, NQKV, NQKV_pad, max_pos;
+  bool rope_half;  // RoPE pairs (i, i + D/2) instead of (2i, 2i+1)
   int d_rows;  // stored rows of W_o and W_down: d, rounded up to 256 for tiled bf16
   DType dt;
   size_t es;
@@ -49,6 +50,7 @@ size_t op_rows(const Shape& s, size_t T) { return s.dt == DType::BF16 ? (T + 255
 llama_status check_config(const llama_layer_config* c, Shape* s) {
   if (!c) return LLAMA_ERR_INVALID_ARG;
   if (c->dtype != LLAMA_DTYPE_F32 && c->dtype != LLAMA_DTYPE_BF16) return LLAMA_ERR_DTYPE;
+  if (c->rope_style != LLAMA_ROPE_INTERLEAVED && c->rope_style != LLAMA_ROPE_HALF_SPLIT) return LLAMA_ERR_INVALID_ARG;
   if (c->hidden_size <= 0 || c->intermediate_size <= 0 || c->num_attention_heads <= 0 ||
       c->num_key_value_heads <= 0 || c->max_position <= 0)
     return LLAMA_ERR_INVALID_ARG;
@@ -82,6 +84,7 @@ llama_status check_config(const llama_layer_config* c, Shape* s) {
   s->dt = c->dtype == LLAMA_DTYPE_BF16 ? DType::BF16 : DType::F32;
   s->es = llk::dsize(s->dt);
   s->d_rows = s->dt == DType::BF16 ? (s->d + 255) / 256 * 256 : s->d;
+  s->rope_half = c->rope_style == LLAMA_ROPE_HALF_SPLIT;
   return LLAMA_OK;
 }
 
@@ -430,20 +433,26 @@ llama_status llama_layer_create(const llama_layer_config* cfg, const llama_layer
   };
   char* P = L->packed;
   hipError_t e = llk::launch_zero(P, L->pl.cos, hs);  // padding rows and columns stay zero
-  // fused QKV weight with gamma_1 folded in: rows [q | k | v]
-  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->q_proj, w->input_layernorm, P + L->pl.qkv, s.HD, s.d, s.d, 1, 0, hs);
+  // fused QKV weight with gamma_1 folded in: rows [q | k | v].  With half-split
+  // RoPE the q and k rows of each head are reordered (0, D/2, 1, D/2+1, ...)
+  // so that every rotated pair sits in adjacent rows, as in the interleaved
+  // form; the QKV epilogue writes each result back to its own position.
+  const int rp = s.rope_half ? s.D : 0;
   if (e == hipSuccess)
-    e = llk::launch_pack(s.dt, w->k_proj, w->input_layernorm, P + L->pl.qkv, s.KD, s.d, s.d, 1, s.HD, hs);
+    e = llk::launch_pack(s.dt, w->q_proj, w->input_layernorm, P + L->pl.qkv, s.HD, s.d, s.d, 1, 0, rp, hs);
   if (e == hipSuccess)
-    e = llk::launch_pack(s.dt, w->v_proj, w->input_layernorm, P + L->pl.qkv, s.KD, s.d, s.d, 1, s.HD + s.KD, hs);
-  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->o_proj, nullptr, P + L->pl.o, s.d, s.HD, s.HD, 1, 0, hs);
+    e = llk::launch_pack(s.dt, w->k_proj, w->input_layernorm, P + L->pl.qkv, s.KD, s.d, s.d, 1, s.HD, rp, hs);
+  if (e == hipSuccess)
+    e = llk::launch_pack(s.dt, w->v_proj, w->input_layernorm, P + L->pl.qkv, s.KD, s.d, s.d, 1, s.HD + s.KD, 0, hs);
+  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->o_proj, nullptr, P + L->pl.o, s.d, s.HD, s.HD, 1, 0, 0, hs);
   // gate/up interleaved row by row; gamma_2 scales the activation instead
   // (h * gamma_2 is rounded once, the weights stay exact)
-  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->gate_proj, nullptr, P + L->pl.gu, s.I, s.d, s.d, 2, 0, hs);
-  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->up_proj, nullptr, P + L->pl.gu, s.I, s.d, s.d, 2, 1, hs);
+  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->gate_proj, nullptr, P + L->pl.gu, s.I, s.d, s.d, 2, 0, 0, hs);
+  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->up_proj, nullptr, P + L->pl.gu, s.I, s.d, s.d, 2, 1, 0, hs);
   if (e == hipSuccess)
     e = llk::launch_to_f32(s.dt, w->post_attention_layernorm, reinterpret_cast<float*>(P + L->pl.gamma2), s.d, hs);
-  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->down_proj, nullptr, P + L->pl.down, s.d, s.I, s.I_pad, 1, 0, hs);
+  if (e == hipSuccess)
+    e = llk::launch_pack(s.dt, w->down_proj, nullptr, P + L->pl.down, s.d, s.I, s.I_pad, 1, 0, 0, hs);
   if (e != hipSuccess) return fail(e);
 
   // RoPE table, angle pos * theta^(-2i/D) evaluated in double, stored fp32
@@ -725,6 +734,7 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
   a.batch = bv;
   a.rope_cos = reinterpret_cast<const float*>(P + L->pl.cos);
   a.rope_sin = reinterpret_cast<const float*>(P + L->pl.sin);
+  a.rope_half = s.rope_half ? 1 : 0;
   a.H = s.H;
   HIP_TRY(timed(L, K_QKV, hs, [&] { return llk::launch_gemm(s.dt, tile_for(a.N), a, hs); }));
 

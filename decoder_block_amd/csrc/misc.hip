@@ -12,12 +12,17 @@ namespace {
 template <typename T>
 __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, const T* __restrict__ gamma,
                                                    T* __restrict__ dst, int rows, int cols, int ldd, int row_mul,
-                                                   int row_add) {
+                                                   int row_add, int head_pairs) {
   const size_t total = (size_t)rows * cols;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
-    const int r = (int)(i / cols), c = (int)(i % cols);
+    int r = (int)(i / cols);
+    const int c = (int)(i % cols);
     float v = to_f32(src[i]);
     if (gamma) v *= to_f32(gamma[c]);
+    if (head_pairs > 0) {  // rows w and w + D/2 of a head become adjacent
+      const int D = head_pairs, w = r % D, half = D / 2;
+      r = r - w + (w < half ? 2 * w : 2 * (w - half) + 1);
+    }
     const int dr = r * row_mul + row_add;
     if constexpr (sizeof(T) == 2)
       dst[tiled_off(dr, c, ldd)] = from_f32<T>(v);
@@ -79,15 +84,17 @@ int grid_for(size_t n) {
 }  // namespace
 
 hipError_t launch_pack(DType t, const void* src, const void* gamma, void* dst, int rows, int cols, int ldd,
-                       int row_mul, int row_add, hipStream_t s) {
+                       int row_mul, int row_add, int head_pairs, hipStream_t s) {
+  if (head_pairs < 0 || head_pairs % 2 != 0 || (head_pairs > 0 && rows % head_pairs != 0)) return hipErrorInvalidValue;
   const int grid = grid_for((size_t)rows * cols);
   if (t == DType::BF16)
     pack_kernel<bf16><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(src), reinterpret_cast<const bf16*>(gamma),
-                                           reinterpret_cast<bf16*>(dst), rows, cols, ldd, row_mul, row_add);
+                                           reinterpret_cast<bf16*>(dst), rows, cols, ldd, row_mul, row_add,
+                                           head_pairs);
   else
     pack_kernel<float><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(src),
                                             reinterpret_cast<const float*>(gamma), reinterpret_cast<float*>(dst),
-                                            rows, cols, ldd, row_mul, row_add);
+                                            rows, cols, ldd, row_mul, row_add, head_pairs);
   return hipGetLastError();
 }
 

@@ -43,7 +43,7 @@ class LlamaLayerConfig(ctypes.Structure):
     _fields_ = [("hidden_size", ctypes.c_int32), ("intermediate_size", ctypes.c_int32),
                 ("num_attention_heads", ctypes.c_int32), ("num_key_value_heads", ctypes.c_int32),
                 ("rms_norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                ("max_position", ctypes.c_int32), ("dtype", ctypes.c_int)]
+                ("max_position", ctypes.c_int32), ("dtype", ctypes.c_int), ("rope_style", ctypes.c_int32)]
 
 
 class LlamaLayerWeights(ctypes.Structure):
@@ -102,12 +102,16 @@ def _check(status: int, where: str):
         raise LlamaError(status, where)
 
 
+ROPE_STYLES = {"interleaved": 0, "half_split": 1}
+
+
 def make_config(hidden_size, intermediate_size, num_attention_heads, num_key_value_heads,
-                rms_norm_eps, rope_theta, max_position, dtype) -> LlamaLayerConfig:
+                rms_norm_eps, rope_theta, max_position, dtype, rope_style="interleaved") -> LlamaLayerConfig:
     dt = {"f32": LLAMA_DTYPE_F32, "bf16": LLAMA_DTYPE_BF16}.get(dtype, dtype)
+    rs = ROPE_STYLES.get(rope_style, rope_style)
     return LlamaLayerConfig(int(hidden_size), int(intermediate_size), int(num_attention_heads),
                             int(num_key_value_heads), float(rms_norm_eps), float(rope_theta),
-                            int(max_position), int(dt))
+                            int(max_position), int(dt), int(rs))
 
 
 def _i32_array(vals):
@@ -254,7 +258,8 @@ class DecoderLayer:
         self.device = torch.device(device)
         self.cfg = make_config(config["hidden_size"], config["intermediate_size"],
                                config["num_attention_heads"], config["num_key_value_heads"],
-                               config["rms_norm_eps"], config["rope_theta"], max_position, dtype)
+                               config["rms_norm_eps"], config["rope_theta"], max_position, dtype,
+                               config.get("rope_style", "interleaved"))
         self.packed = _dev_bytes(llama_layer_packed_bytes(self.cfg), self.device)
         src = {k: v.to(self.device, self.tdtype).contiguous() for k, v in weights.items()}
         w = LlamaLayerWeights(*[src[n].data_ptr() for n in

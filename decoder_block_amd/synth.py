@@ -55,6 +55,7 @@ class Workload:
     ctx_hi: int = 0
     block_size: int = 16
     max_position: int = 0      # RoPE table length; 0: derived from the job
+    rope_style: str = "interleaved"  # or "half_split": which head elements RoPE pairs
 
     @property
     def head_dim(self) -> int:
@@ -75,7 +76,8 @@ class Workload:
                     num_attention_heads=self.num_attention_heads,
                     num_key_value_heads=self.num_key_value_heads,
                     rms_norm_eps=self.rms_norm_eps,
-                    rope_theta=self.rope_theta)
+                    rope_theta=self.rope_theta,
+                    rope_style=self.rope_style)
 
 
 WORKLOADS = {

@@ -15,9 +15,11 @@
  *     fields used below);
  *   - RMSNorm(x) = x * rsqrt(mean(x^2) + eps) * gamma, in fp32
  *     ("Chapter 10", section 4; "3.2 Core components, one by one", 3.2.1);
- *   - RoPE on q and k only, interleaved pairs (x[2i], x[2i+1]) rotated by
- *     pos * theta^(-2i/D) ("Chapter 10", sections 2-3; "From Transformer to
- *     LLaMA: an overview", 4.2);
+ *   - RoPE on q and k only, pair i rotated by pos * theta^(-2i/D) ("Chapter
+ *     10", sections 2-3; "From Transformer to LLaMA: an overview", 4.2), the
+ *     pairs being interleaved (x[2i], x[2i+1]) ("Chapter 10", section 3) or,
+ *     as an option, the two halves of the head (x[i], x[i + D/2]) ("From
+ *     Transformer to the LLaMA series", section 8, apply_rope);
  *   - grouped-query attention: query head h reads KV head h / (H/G); the
  *     cache stores only the G KV heads ("Chapter 10", section 6);
  *   - softmax(q k^T / sqrt(D)) v with a causal mask, diagonal included
@@ -79,6 +81,13 @@ typedef enum {
 
 typedef enum { LLAMA_DTYPE_F32 = 0, LLAMA_DTYPE_BF16 = 1 } llama_dtype;
 
+/* Which elements of a head RoPE rotates together (same angle pos * theta^(-2i/D)
+ * for pair i in both). */
+typedef enum {
+  LLAMA_ROPE_INTERLEAVED = 0, /* (x[2i], x[2i+1]): "Chapter 10", section 3 */
+  LLAMA_ROPE_HALF_SPLIT = 1   /* (x[i], x[i + D/2]): "From Transformer to the LLaMA series", section 8 */
+} llama_rope_style;
+
 /* The config.json fields of the layer ("Chapter 10", section 1) plus the
  * storage dtype and the RoPE table length.  Accumulation is always fp32.
  * Supported: head_dim D = hidden_size / num_attention_heads in {64, 128}
@@ -94,6 +103,7 @@ typedef struct {
   float rope_theta;
   int32_t max_position; /* positions >= max_position are rejected (LLAMA_ERR_POSITION) */
   int32_t dtype;        /* a llama_dtype: weights, activations and cache */
+  int32_t rope_style;   /* a llama_rope_style (other values: LLAMA_ERR_INVALID_ARG) */
 } llama_layer_config;
 
 /* Device pointers to the nine parameter tensors, nn.Linear layout. */

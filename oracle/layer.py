@@ -27,8 +27,9 @@ Readings taken where the pages are silent or disagree:
   * eps sits inside the square root: rsqrt(mean(x^2) + eps) (the code on
     P1/P2/P3/P4; P2's displayed formula with eps outside is taken as a typo).
   * RoPE pairs are interleaved (2i, 2i+1) with angle pos * theta^(-2i/D), D the
-    head dimension (P3 section 3, P4 section 4.2); P1's half-split variant is
-    not this layer.
+    head dimension (P3 section 3, P4 section 4.2).  P1's half-split variant
+    (pairs (i, i + D/2), same angles) is an option: cfg["rope_style"] =
+    "half_split".
   * softmax scale is 1/sqrt(D); query head h reads KV head floor(h / (H/G)).
   * key j is visible to a query iff pos_j <= pos_q (diagonal included); a
     decoded token sits at position = current cache length and is appended to
@@ -71,11 +72,13 @@ def rope_inv_freq(head_dim: int, theta: float) -> np.ndarray:
     return theta ** (-2.0 * i / head_dim)
 
 
-def apply_rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
-    """Rotate interleaved pairs (x[2i], x[2i+1]) of every head by pos * theta_i.
+def apply_rope(x: np.ndarray, positions: np.ndarray, theta: float, style: str = "interleaved") -> np.ndarray:
+    """Rotate the pairs of every head by pos * theta_i.
 
     x: [T, heads, D]; positions: [T] absolute positions.
-    new_even = e cos - o sin, new_odd = e sin + o cos  ([P3] section 3).
+    interleaved ([P3] section 3): pair i = (x[2i], x[2i+1]);
+    half_split ([P1] section 8, apply_rope): pair i = (x[i], x[i + D/2]).
+    For a pair (e, o): new_e = e cos - o sin, new_o = e sin + o cos.
     """
     D = x.shape[-1]
     if D % 2:
@@ -83,11 +86,20 @@ def apply_rope(x: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray
     ang = np.asarray(positions, dtype=np.float64)[:, None] * rope_inv_freq(D, theta)[None, :]
     c = np.cos(ang)[:, None, :]
     s = np.sin(ang)[:, None, :]
-    e, o = x[..., 0::2], x[..., 1::2]
-    y = np.empty_like(x)
-    y[..., 0::2] = e * c - o * s
-    y[..., 1::2] = e * s + o * c
-    return y
+    if style == "interleaved":
+        e, o = x[..., 0::2], x[..., 1::2]
+    elif style == "half_split":
+        e, o = x[..., : D // 2], x[..., D // 2:]
+    else:
+        raise ValueError(f"unknown RoPE style {style!r}")
+    new_e = e * c - o * s
+    new_o = e * s + o * c
+    if style == "interleaved":
+        y = np.empty_like(x)
+        y[..., 0::2] = new_e
+        y[..., 1::2] = new_o
+        return y
+    return np.concatenate([new_e, new_o], axis=-1)
 
 
 def causal_gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
@@ -144,7 +156,8 @@ def project_kv(cfg: dict, w: dict, x: np.ndarray, positions: np.ndarray):
     """K (rotated) and V of tokens x [T, d] at the given positions: ([T,G,D], [T,G,D])."""
     G = cfg["num_key_value_heads"]
     n1 = rms_norm(x, w["input_layernorm"], cfg["rms_norm_eps"])
-    k = apply_rope(_split_heads(linear(n1, w["k_proj"]), G), positions, cfg["rope_theta"])
+    k = apply_rope(_split_heads(linear(n1, w["k_proj"]), G), positions, cfg["rope_theta"],
+                   cfg.get("rope_style", "interleaved"))
     v = _split_heads(linear(n1, w["v_proj"]), G)
     return k, v
 
@@ -158,7 +171,8 @@ def attention_block(cfg: dict, w: dict, x: np.ndarray, positions: np.ndarray,
     """
     H = cfg["num_attention_heads"]
     n1 = rms_norm(x, w["input_layernorm"], cfg["rms_norm_eps"])
-    q = apply_rope(_split_heads(linear(n1, w["q_proj"]), H), positions, cfg["rope_theta"])
+    q = apply_rope(_split_heads(linear(n1, w["q_proj"]), H), positions, cfg["rope_theta"],
+                   cfg.get("rope_style", "interleaved"))
     a = causal_gqa_attention(q, k_all, v_all, positions, k_pos)
     return x + linear(a.reshape(x.shape[0], -1), w["o_proj"])
 

@@ -25,7 +25,7 @@ static int g_fail = 0;
 static std::vector<std::string> g_log;
 static int g_events = 0;
 static int g_uploads = 0;
-struct PackCall { int rows, cols, ldd, row_mul, row_add; bool gamma; };
+struct PackCall { int rows, cols, ldd, row_mul, row_add, head_pairs; bool gamma; };
 static std::vector<PackCall> g_packs;
 
 namespace llk {
@@ -86,8 +86,8 @@ hipError_t event_elapsed_ms(float* ms, void*, void*) {
   return hipSuccess;
 }
 hipError_t launch_pack(DType, const void*, const void* gamma, void*, int rows, int cols, int ldd, int row_mul,
-                       int row_add, hipStream_t) {
-  g_packs.push_back({rows, cols, ldd, row_mul, row_add, gamma != nullptr});
+                       int row_add, int head_pairs, hipStream_t) {
+  g_packs.push_back({rows, cols, ldd, row_mul, row_add, head_pairs, gamma != nullptr});
   return hipSuccess;
 }
 hipError_t launch_to_f32(DType, const void*, float* dst, int n, hipStream_t) {
@@ -150,6 +150,7 @@ static llama_layer_config tiny(llama_dtype dt = LLAMA_DTYPE_F32) {
   c.rope_theta = 10000.f;
   c.max_position = 80;
   c.dtype = dt;
+  c.rope_style = LLAMA_ROPE_INTERLEAVED;
   return c;
 }
 
@@ -202,6 +203,23 @@ int main() {
     CHECK(g_packs[4].row_mul == 2 && g_packs[4].row_add == 0 && !g_packs[4].gamma);
     CHECK(g_packs[5].row_mul == 2 && g_packs[5].row_add == 1 && !g_packs[5].gamma);
     CHECK(g_packs[6].cols == 688 && g_packs[6].ldd == 768 && !g_packs[6].gamma);
+    for (const PackCall& pc : g_packs) CHECK(pc.head_pairs == 0);  // interleaved RoPE: rows in order
+  }
+  // half-split RoPE: the q and k rows of each head are reordered, nothing else
+  {
+    llama_layer_config ch = c;
+    ch.rope_style = 7;
+    CHECK(llama_layer_packed_bytes(&ch, &bytes) == LLAMA_ERR_INVALID_ARG);
+    ch.rope_style = LLAMA_ROPE_HALF_SPLIT;
+    g_packs.clear();
+    llama_layer* Lh = nullptr;
+    CHECK(llama_layer_create(&ch, &w, packed, nullptr, &Lh) == LLAMA_OK && Lh != nullptr);
+    CHECK(g_packs.size() == 7);
+    if (g_packs.size() == 7) {
+      CHECK(g_packs[0].head_pairs == 64 && g_packs[1].head_pairs == 64);
+      for (int i = 2; i < 7; ++i) CHECK(g_packs[i].head_pairs == 0);
+    }
+    CHECK(llama_layer_destroy(Lh) == LLAMA_OK);
   }
   // the RoPE tables are the last two sections of the packed buffer
   {

@@ -66,6 +66,7 @@ def test_packed_bytes_cover_the_weights(L):
     (dict(rope_theta=float("nan")), "LLAMA_ERR_INVALID_ARG"),
     (dict(max_position=0), "LLAMA_ERR_INVALID_ARG"),
     (dict(dtype=5), "LLAMA_ERR_DTYPE"),
+    (dict(rope_style=2), "LLAMA_ERR_INVALID_ARG"),
 ])
 def test_config_validation(L, kw, status):
     with pytest.raises(L.LlamaError) as e:

@@ -251,3 +251,48 @@ def test_bf16_output_dtype():
     b, _ = P.gpu_prefill(layer, P.make_cache(layer, w, 64, 1), x, out_dtype="bf16")
     assert b.dtype == torch.bfloat16
     assert torch.equal(a.to(torch.bfloat16), b)
+
+
+# ----------------------------------------------------------------------------
+# half-split RoPE (pairs (i, i + D/2)), a create-time option of the layer
+# ----------------------------------------------------------------------------
+
+def test_half_split_rope_tiny_fp32_prefill_decode_and_cache():
+    w = synth.scaled(W[1], rope_style="half_split")
+    ws, wo = P.weights_for(w)
+    x = synth.layer_input(w)
+    layer = P.make_layer(w, ws)
+    cache = P.make_cache(layer, w, w.seq_len + 3, 1, block_order_seed=2)
+    out, sids = P.gpu_prefill(layer, cache, x)
+    ref, k_ref, v_ref = oracle.prefill(_cfg(w), wo, synth.as_f64(x))
+    P.assert_close(P.to_np(out), ref, "f32", "half-split prefill")
+    k, v = cache.read(sids[0], 0, w.seq_len)
+    P.assert_close(P.to_np(k), k_ref[0], "f32", "half-split cached K")
+    P.assert_close(P.to_np(v), v_ref[0], "f32", "half-split cached V")
+    caches = [(k_ref[0], v_ref[0])]
+    for step in range(3):
+        xt = synth.decode_input(w, step)
+        o = layer.decode(cache, sids, xt.cuda())
+        torch.cuda.synchronize()
+        r, caches = oracle.decode_step(_cfg(w), wo, synth.as_f64(xt), caches)
+        P.assert_close(P.to_np(o), r, "f32", f"half-split decode step {step}")
+
+
+def test_half_split_rope_bf16_prefill_and_decode():
+    w = synth.scaled(W[3], batch=2, seq_len=300, rope_style="half_split")
+    ws, wo = P.weights_for(w)
+    x = synth.layer_input(w)
+    layer = P.make_layer(w, ws)
+    cache = P.make_cache(layer, w, w.seq_len + 16, w.batch, block_order_seed=4)
+    out, sids = P.gpu_prefill(layer, cache, x)
+    ref, k_ref, v_ref = oracle.prefill(_cfg(w), wo, synth.as_f64(x))
+    e = P.assert_close(P.to_np(out), ref, "bf16", "half-split bf16 prefill")
+    print("half-split prefill", e)
+    k, _ = cache.read(sids[1], 0, w.seq_len)
+    P.assert_close(P.to_np(k), k_ref[1], "bf16", "half-split cached K")
+    # one decode step over both sequences (the few-token GEMM path)
+    xt = synth.decode_input(w, 0)
+    o = layer.decode(cache, sids, xt.cuda())
+    torch.cuda.synchronize()
+    r, _ = oracle.decode_step(_cfg(w), wo, synth.as_f64(xt), [(k_ref[b], v_ref[b]) for b in range(w.batch)])
+    P.assert_close(P.to_np(o), r, "bf16", "half-split decode")

@@ -127,6 +127,48 @@ def test_rope_scores_depend_only_on_offset():
         assert val == pytest.approx(math.cos(m - n), abs=1e-14)
 
 
+@pytest.mark.parametrize("p", [0, 1, 5, 1000])
+def test_rope_half_split_pairs_and_frequencies(p):
+    # "From Transformer to the LLaMA series", section 8 (apply_rope): x1 = first
+    # half, x2 = second half, result [x1 cos - x2 sin, x2 cos + x1 sin], angle
+    # pos * theta^(-2i/D) for element i of a half
+    theta = 10000.0
+    e = np.eye(4)[:, None, :]
+    y = oracle.apply_rope(e, np.full(4, p), theta, "half_split")[:, 0, :]
+    a0, a1 = p * 1.0, p * theta ** (-2.0 / 4)
+    c0, s0, c1, s1 = math.cos(a0), math.sin(a0), math.cos(a1), math.sin(a1)
+    # pair (0, 2) rotates by a0 and pair (1, 3) by a1
+    np.testing.assert_allclose(y[0], [c0, 0, s0, 0], atol=1e-15)
+    np.testing.assert_allclose(y[1], [0, c1, 0, s1], atol=1e-15)
+    np.testing.assert_allclose(y[2], [-s0, 0, c0, 0], atol=1e-15)
+    np.testing.assert_allclose(y[3], [0, -s1, 0, c1], atol=1e-15)
+
+
+def test_rope_half_split_is_interleaved_in_reordered_coordinates():
+    # reordering a head's elements as (0, D/2, 1, D/2+1, ...) turns the
+    # half-split pairs into interleaved ones with the same angles
+    D = 16
+    perm = np.ravel(np.stack([np.arange(D // 2), np.arange(D // 2) + D // 2], axis=1))
+    x = rng.standard_normal((6, 3, D))
+    pos = np.array([0, 1, 2, 50, 999, 8191])
+    half = oracle.apply_rope(x, pos, 500000.0, "half_split")
+    inter = oracle.apply_rope(x[..., perm], pos, 500000.0)
+    np.testing.assert_allclose(half[..., perm], inter, rtol=1e-14, atol=1e-14)
+
+
+def test_rope_half_split_preserves_norms_and_depends_on_offset_only():
+    x = rng.standard_normal((20, 2, 64))
+    pos = rng.integers(0, 8192, size=20)
+    y = oracle.apply_rope(x, pos, 500000.0, "half_split")
+    np.testing.assert_allclose(y[..., :32] ** 2 + y[..., 32:] ** 2, x[..., :32] ** 2 + x[..., 32:] ** 2, rtol=1e-12)
+    q, k = rng.standard_normal((1, 1, 64)), rng.standard_normal((1, 1, 64))
+    def score(m, n):
+        return float(np.sum(oracle.apply_rope(q, np.array([m]), 1e4, "half_split") *
+                            oracle.apply_rope(k, np.array([n]), 1e4, "half_split")))
+    for m, n, sh in [(5, 2, 100), (9, 30, 17)]:
+        assert score(m, n) == pytest.approx(score(m + sh, n + sh), rel=1e-10, abs=1e-10)
+
+
 def test_rope_rejects_odd_head_dim():
     with pytest.raises(ValueError):
         oracle.apply_rope(np.zeros((1, 1, 3)), np.array([0]), 1e4)
@@ -299,6 +341,7 @@ def test_values_are_not_rotated():
 
 def _brute_layer(cfg, w, x):
     """Scalar-loop decoder layer for one short sequence from empty cache."""
+    half = cfg.get("rope_style", "interleaved") == "half_split"
     d, I = cfg["hidden_size"], cfg["intermediate_size"]
     H, G = cfg["num_attention_heads"], cfg["num_key_value_heads"]
     D, eps, th = d // H, cfg["rms_norm_eps"], cfg["rope_theta"]
@@ -317,9 +360,11 @@ def _brute_layer(cfg, w, x):
         for hd in range(len(vec) // D):
             for i in range(D // 2):
                 a = p * th ** (-2.0 * i / D)
-                e, o = vec[hd * D + 2 * i], vec[hd * D + 2 * i + 1]
-                out[hd * D + 2 * i] = e * math.cos(a) - o * math.sin(a)
-                out[hd * D + 2 * i + 1] = e * math.sin(a) + o * math.cos(a)
+                # pair i: interleaved (2i, 2i+1), or the two halves (i, i + D/2)
+                ie, io = (hd * D + i, hd * D + i + D // 2) if half else (hd * D + 2 * i, hd * D + 2 * i + 1)
+                e, o = vec[ie], vec[io]
+                out[ie] = e * math.cos(a) - o * math.sin(a)
+                out[io] = e * math.sin(a) + o * math.cos(a)
         return out
 
     xs = [list(r) for r in x]
@@ -344,9 +389,10 @@ def _brute_layer(cfg, w, x):
     return np.array(outs)
 
 
-@pytest.mark.parametrize("H,G", [(4, 2), (2, 2), (4, 1)])
-def test_layer_matches_scalar_brute_force(H, G):
-    cfg = _tiny_cfg(H=H, G=G, d=16, I=12)
+@pytest.mark.parametrize("H,G,style", [(4, 2, "interleaved"), (2, 2, "interleaved"), (4, 1, "interleaved"),
+                                       (4, 2, "half_split")])
+def test_layer_matches_scalar_brute_force(H, G, style):
+    cfg = dict(_tiny_cfg(H=H, G=G, d=16, I=12), rope_style=style)
     w = _tiny_weights(cfg, seed=H * 10 + G)
     x = rng.standard_normal((5, 16))
     out, _, _ = oracle.layer_forward(cfg, w, x)
