@@ -8,8 +8,9 @@
 // of the batch is read once per KV group, shared by the R = H/G query heads.
 //
 // Split kernel: a workgroup (4 waves) takes one (sequence, group, chunk of
-// 1024 keys); each wave walks 32-key steps (two 16-key cache blocks) and
-// runs both products on 16x16 MFMAs with the R heads as the 16 columns:
+// 1024 keys) and up to 16 of the group's query heads (two workgroups per
+// chunk at R = 32); each wave walks 32-key steps (two 16-key cache blocks)
+// and runs both products on 16x16 MFMAs with the heads as the 16 columns:
 //   S^T [16 keys x heads] = K_block [16 x D] * Q^T   (K loaded straight from HBM)
 //   O^T [D x heads]      += V_block^T [D x 32 keys] * P^T
 // V is kept transposed per block in the cache, so the A operand of the second
@@ -63,7 +64,12 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restr
 
   const int G = cache.G;
   const int R = H / G;
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  // workgroup -> (sequence b, KV group g, 16-head subset sub of the group's R
+  // query heads): a group with more than 16 heads (R = 32, MQA at 32 heads)
+  // takes one workgroup per subset, each reading the group's K/V
+  const int nsub = (R + 15) / 16;
+  const int b = blockIdx.x / (G * nsub), g = (blockIdx.x / nsub) % G, hsub = blockIdx.x % nsub;
+  const int h0 = g * R + 16 * hsub, RS = min(16, R - 16 * hsub);  // first head, heads in the subset
   const int split = blockIdx.y;
   const int seq = batch.desc[2 * b];
   const int kv_len = batch.desc[2 * b + 1] + 1;
@@ -75,13 +81,13 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restr
   const int c16 = lane & 15, g4 = lane >> 4;
   const int HD = H * D;
 
-  // Q^T fragments: column c16 = query head g*R + c16 (zero for c16 >= R)
+  // Q^T fragments: column c16 = query head h0 + c16 (zero for c16 >= RS)
   vec qf[C::NQK];
   {
-    const T* qp = q + (size_t)b * HD + (size_t)(g * R + c16) * D;
+    const T* qp = q + (size_t)b * HD + (size_t)(h0 + c16) * D;
 #pragma unroll
     for (int s = 0; s < C::NQK; ++s)
-      qf[s] = c16 < R ? load_chunk<T>(qp + (4 * s + g4) * C::CH) : zero_chunk<T>();
+      qf[s] = c16 < RS ? load_chunk<T>(qp + (4 * s + g4) * C::CH) : zero_chunk<T>();
   }
 
   const T* kpool = reinterpret_cast<const T*>(cache.k_pool);
@@ -195,14 +201,14 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restr
   __syncthreads();
   // 256 threads: head hh = tid / 16 (16 heads), 16 threads per head over D + 2 values
   const int hh = tid >> 4, sub = tid & 15;
-  if (hh >= R) return;
+  if (hh >= RS) return;
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][hh][0]);
   float f[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) f[w] = exp2f(sm[w][hh][0] - M);  // waves without keys: exp2(-inf) = 0
-  float* dst = part + (((size_t)b * H + g * R + hh) * max_splits + split) * (D + 2);
+  float* dst = part + (((size_t)b * H + h0 + hh) * max_splits + split) * (D + 2);
   for (int x = sub; x < D + 2; x += 16) {
     float v;
     if (x == 0) {
@@ -270,7 +276,12 @@ __global__ __launch_bounds__(256, 3) void attn_decode_wave_kernel(const bf16* __
   __shared__ float sm[4][16][D + 2];
   const int G = cache.G;
   const int R = H / G;
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  // workgroup -> (sequence b, KV group g, 16-head subset sub of the group's R
+  // query heads): a group with more than 16 heads (R = 32, MQA at 32 heads)
+  // takes one workgroup per subset, each reading the group's K/V
+  const int nsub = (R + 15) / 16;
+  const int b = blockIdx.x / (G * nsub), g = (blockIdx.x / nsub) % G, hsub = blockIdx.x % nsub;
+  const int h0 = g * R + 16 * hsub, RS = min(16, R - 16 * hsub);  // first head, heads in the subset
   const int split = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -284,9 +295,9 @@ __global__ __launch_bounds__(256, 3) void attn_decode_wave_kernel(const bf16* __
   const int c16 = lane & 15, g4 = lane >> 4;
   bf16x8 qf[D / 32];
   {
-    const bf16* qp = q + (size_t)b * H * D + (size_t)(g * R + c16) * D;
+    const bf16* qp = q + (size_t)b * H * D + (size_t)(h0 + c16) * D;
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) qf[s] = c16 < R ? load_chunk<bf16>(qp + (4 * s + g4) * 8) : zero_chunk<bf16>();
+    for (int s = 0; s < D / 32; ++s) qf[s] = c16 < RS ? load_chunk<bf16>(qp + (4 * s + g4) * 8) : zero_chunk<bf16>();
   }
   const int32_t* btab = cache.block_table + (size_t)seq * cache.max_blocks + (k_begin >> 4);
   const bf16* kpool = reinterpret_cast<const bf16*>(cache.k_pool);
@@ -361,14 +372,14 @@ __global__ __launch_bounds__(256, 3) void attn_decode_wave_kernel(const bf16* __
   }
   __syncthreads();
   const int hh = tid >> 4, sub = tid & 15;
-  if (hh >= R) return;
+  if (hh >= RS) return;
   float M = -INFINITY;
 #pragma unroll
   for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][hh][0]);
   float f[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) f[w] = fast_exp2(sm[w][hh][0] - M);  // waves without keys: exp2(-inf) = 0
-  float* dst = part + (((size_t)b * H + g * R + hh) * max_splits + split) * (D + 2);
+  float* dst = part + (((size_t)b * H + h0 + hh) * max_splits + split) * (D + 2);
   for (int x = sub; x < D + 2; x += 16) {
     float v;
     if (x == 0) {
@@ -418,7 +429,7 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* _
 template <typename T, int D>
 hipError_t launch_split(const void* q, float* part, int max_splits, int H, const CacheView& c, const BatchView& b,
                         hipStream_t s) {
-  dim3 grid(c.G * b.batch, max_splits);
+  dim3 grid(c.G * ((H / c.G + 15) / 16) * b.batch, max_splits);
   attn_decode_split_kernel<T, D><<<grid, 256, 0, s>>>(reinterpret_cast<const T*>(q), part, max_splits, H, c, b);
   return hipGetLastError();
 }
@@ -436,9 +447,9 @@ int decode_split_keys() { return kChunkKeys; }
 
 hipError_t launch_attn_decode(DType t, const void* q, float* partial, int max_splits, int H, const CacheView& c,
                               const BatchView& b, hipStream_t s) {
-  if (H % c.G != 0 || H / c.G > 16) return hipErrorInvalidValue;
+  if (H % c.G != 0 || H / c.G > 32) return hipErrorInvalidValue;
   if (t == DType::BF16) {
-    dim3 grid(c.G * b.batch, max_splits);
+    dim3 grid(c.G * ((H / c.G + 15) / 16) * b.batch, max_splits);
     if (c.D == 128)
       attn_decode_wave_kernel<128><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(q), partial, max_splits, H, c, b);
     else if (c.D == 64)

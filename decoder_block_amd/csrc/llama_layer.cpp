@@ -65,7 +65,7 @@ llama_status check_config(const llama_layer_config* c, Shape* s) {
   if (D != 64 && D != 128) return LLAMA_ERR_UNSUPPORTED;
   if (c->dtype == LLAMA_DTYPE_F32 && D != 64) return LLAMA_ERR_UNSUPPORTED;
   const int R = c->num_attention_heads / c->num_key_value_heads;
-  if (R > 16 || (R & (R - 1)) != 0) return LLAMA_ERR_UNSUPPORTED;
+  if (R > 32 || (R & (R - 1)) != 0) return LLAMA_ERR_UNSUPPORTED;
   if (c->hidden_size % 64 != 0 || c->intermediate_size % 8 != 0) return LLAMA_ERR_SHAPE;
   if ((int64_t)c->hidden_size > (1 << 16) || (int64_t)c->intermediate_size > (1 << 18) ||
       c->max_position > (1 << 22))

@@ -92,7 +92,7 @@ typedef enum {
  * storage dtype and the RoPE table length.  Accumulation is always fp32.
  * Supported: head_dim D = hidden_size / num_attention_heads in {64, 128}
  * (fp32 layers: 64),
- * num_attention_heads / num_key_value_heads in {1, 2, 4, 8, 16},
+ * num_attention_heads / num_key_value_heads in {1, 2, 4, 8, 16, 32},
  * hidden_size a multiple of 64, intermediate_size a multiple of 8. */
 typedef struct {
   int32_t hidden_size;

@@ -61,7 +61,7 @@ def test_packed_bytes_cover_the_weights(L):
     (dict(num_key_value_heads=3), "LLAMA_ERR_SHAPE"),          # H % G != 0
     (dict(hidden_size=4100), "LLAMA_ERR_SHAPE"),               # d % H != 0
     (dict(hidden_size=96 * 32), "LLAMA_ERR_UNSUPPORTED"),      # head_dim 96
-    (dict(num_attention_heads=64, num_key_value_heads=2, hidden_size=8192), "LLAMA_ERR_UNSUPPORTED"),  # R = 32
+    (dict(num_attention_heads=128, num_key_value_heads=2, hidden_size=8192), "LLAMA_ERR_UNSUPPORTED"),  # R = 64
     (dict(rms_norm_eps=0.0), "LLAMA_ERR_INVALID_ARG"),
     (dict(rope_theta=float("nan")), "LLAMA_ERR_INVALID_ARG"),
     (dict(max_position=0), "LLAMA_ERR_INVALID_ARG"),

@@ -296,3 +296,81 @@ def test_half_split_rope_bf16_prefill_and_decode():
     torch.cuda.synchronize()
     r, _ = oracle.decode_step(_cfg(w), wo, synth.as_f64(xt), [(k_ref[b], v_ref[b]) for b in range(w.batch)])
     P.assert_close(P.to_np(o), r, "bf16", "half-split decode")
+
+
+# ----------------------------------------------------------------------------
+# GQA ratio sweep: MQA (one K/V head shared by all 32 query heads) and the
+# LLaMA-3-405B layer shape (d 16384, 128 query heads over 8 K/V heads, I 53248)
+# ----------------------------------------------------------------------------
+
+def test_mqa_bf16_prefill_and_cache():
+    w = synth.scaled(W[3], num_key_value_heads=1, batch=2, seq_len=300)
+    got, ref, (layer, cache, sids, k_ref, v_ref) = _prefill_case(w, block_seed=6)
+    e = P.assert_close(got, ref, "bf16", "MQA prefill")
+    print("MQA prefill", e)
+    k, v = cache.read(sids[1], 0, w.seq_len)
+    P.assert_close(P.to_np(k), k_ref[1], "bf16", "MQA cached K")
+    P.assert_close(P.to_np(v), v_ref[1], "bf16", "MQA cached V")
+
+
+def test_mqa_decode_ragged_lengths_two_steps():
+    # 32 query heads on one K/V head: two 16-head workgroups per key chunk
+    w = synth.scaled(W[4], num_key_value_heads=1, batch=5)
+    layer, cache, sids, host, wo = _decode_setup(w, lens=[1, 16, 333, 1024, 2049], block_seed=8)
+    for step in range(2):
+        xt = synth.decode_input(w, step)
+        o = layer.decode(cache, sids, xt.cuda())
+        torch.cuda.synchronize()
+        ref, host = oracle.decode_step(_cfg(w), wo, synth.as_f64(xt), host)
+        e = P.assert_close(P.to_np(o), ref, "bf16", f"MQA decode step {step}")
+        print("MQA decode step", step, e)
+
+
+def test_mqa_tiny_fp32_prefill_and_decode():
+    # head_dim 64, 32 query heads on one K/V head
+    w = synth.scaled(W[1], hidden_size=2048, num_attention_heads=32, num_key_value_heads=1, seq_len=200)
+    ws, wo = P.weights_for(w)
+    x = synth.layer_input(w)
+    layer = P.make_layer(w, ws)
+    cache = P.make_cache(layer, w, w.seq_len + 2, 1, block_order_seed=1)
+    out, sids = P.gpu_prefill(layer, cache, x)
+    ref, k_ref, v_ref = oracle.prefill(_cfg(w), wo, synth.as_f64(x))
+    P.assert_close(P.to_np(out), ref, "f32", "MQA fp32 prefill")
+    caches = [(k_ref[0], v_ref[0])]
+    for step in range(2):
+        xt = synth.decode_input(w, step)
+        o = layer.decode(cache, sids, xt.cuda())
+        torch.cuda.synchronize()
+        r, caches = oracle.decode_step(_cfg(w), wo, synth.as_f64(xt), caches)
+        P.assert_close(P.to_np(o), r, "f32", f"MQA fp32 decode step {step}")
+
+
+LLAMA3_405B = synth.scaled(W[5], hidden_size=16384, intermediate_size=53248, num_attention_heads=128,
+                           num_key_value_heads=8, batch=2, seq_len=300)
+
+
+def test_llama3_405b_layer_prefill_sampled_rows_and_decode():
+    # 3.2 G parameters: built here rather than through the shared weight cache
+    # so that they are released when the test ends
+    w = LLAMA3_405B
+    ws = synth.layer_weights(w)
+    wo = {k: synth.as_f64(v) for k, v in ws.items()}
+    layer = P.make_layer(w, ws)
+    del ws
+    x = synth.layer_input(w)
+    cache = P.make_cache(layer, w, w.seq_len + 1, w.batch, block_order_seed=12)
+    out, sids = P.gpu_prefill(layer, cache, x)
+    rows = synth.sample_rows(w, w.seq_len, n_random=24, edge=8)
+    ref, k_ref, v_ref = oracle.prefill(_cfg(w), wo, synth.as_f64(x), rows=rows)
+    e = P.assert_close(P.to_np(out)[:, rows], ref, "bf16", "405B prefill")
+    print("405B prefill", len(rows), "rows/seq", e)
+    k, v = cache.read(sids[1], 0, w.seq_len)
+    P.assert_close(P.to_np(k), k_ref[1], "bf16", "405B cached K")
+    P.assert_close(P.to_np(v), v_ref[1], "bf16", "405B cached V")
+    # one decode step after the prefill (both sequences at 301 tokens)
+    xt = synth.decode_input(w, 0)
+    o = layer.decode(cache, sids, xt.cuda())
+    torch.cuda.synchronize()
+    r, _ = oracle.decode_step(_cfg(w), wo, synth.as_f64(xt), [(k_ref[b], v_ref[b]) for b in range(w.batch)])
+    e = P.assert_close(P.to_np(o), r, "bf16", "405B decode")
+    print("405B decode", e)
