@@ -8,6 +8,11 @@ pre-filled at context lengths drawn from U[512, 8192]), reported under
 "decode".  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
+                    [--prefill-workload NAME] [--decode-workload NAME]
+
+The workload options time the other shapes with the same step definition:
+the LLaMA-2-7B (MHA) and LLaMA-3-70B layers, and the GQA ratio sweep (MQA at
+the 8B shape, the LLaMA-3-405B layer); the defaults are the 8B jobs above.
 """
 from __future__ import annotations
 
@@ -72,7 +77,7 @@ def prefill_flops(w) -> dict:
 
 
 def run_prefill(args, torch, L, synth):
-    w = synth.WORKLOADS[3]
+    w = synth.PREFILL_JOBS[args.prefill_workload]
     log(f"[bench] prefill workload {w.name}: generating weights")
     ws = synth.layer_weights(w)
     layer = L.DecoderLayer(w.config_dict(), ws, "bf16", w.positions_needed())
@@ -127,7 +132,7 @@ def run_prefill(args, torch, L, synth):
 
 
 def run_decode(args, torch, L, synth):
-    w = synth.WORKLOADS[4]
+    w = synth.DECODE_JOBS[args.decode_workload]
     log(f"[bench] decode workload {w.name}: weights and cache")
     ws = synth.layer_weights(w)
     # positions for the warm-up, timed and profiled steps past the longest context
@@ -236,6 +241,7 @@ def cpu_baseline(synth, w, n_rows: int):
 
 
 def main():
+    from decoder_block_amd import synth
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -245,6 +251,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows (>= S: the whole layer)")
+    ap.add_argument("--prefill-workload", default="llama3-8b-layer-prefill", choices=sorted(synth.PREFILL_JOBS))
+    ap.add_argument("--decode-workload", default="llama3-8b-layer-decode", choices=sorted(synth.DECODE_JOBS))
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -253,7 +261,6 @@ def main():
 
     import torch
     from decoder_block_amd import llama_layer as L
-    from decoder_block_amd import synth
     L.lib()
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

@@ -99,6 +99,27 @@ def scaled(w: Workload, **kw) -> Workload:
     return replace(w, **kw)
 
 
+# The GQA ratio sweep: the LLaMA-3-8B jobs with one K/V head for all 32 query
+# heads (MQA), and the LLaMA-3-405B layer shape (d 16384, 128 query heads over
+# 8 K/V heads, I 53248).  Same recipes and seeds as the jobs they derive from.
+_L405 = dict(hidden_size=16384, intermediate_size=53248, num_attention_heads=128, num_key_value_heads=8,
+             w_std=0.01)
+VARIANTS = {
+    "llama3-8b-mqa-layer-prefill": replace(WORKLOADS[3], name="llama3-8b-mqa-layer-prefill",
+                                           num_key_value_heads=1),
+    "llama3-8b-mqa-layer-decode": replace(WORKLOADS[4], name="llama3-8b-mqa-layer-decode",
+                                          num_key_value_heads=1),
+    "llama3-405b-layer-prefill": replace(WORKLOADS[5], name="llama3-405b-layer-prefill", batch=1,
+                                         seq_len=8192, **_L405),
+    "llama3-405b-layer-decode": replace(WORKLOADS[4], name="llama3-405b-layer-decode", **_L405),
+}
+PREFILL_JOBS = {w.name: w for w in (WORKLOADS[2], WORKLOADS[3], WORKLOADS[5],
+                                    VARIANTS["llama3-8b-mqa-layer-prefill"],
+                                    VARIANTS["llama3-405b-layer-prefill"])}
+DECODE_JOBS = {w.name: w for w in (WORKLOADS[4], VARIANTS["llama3-8b-mqa-layer-decode"],
+                                   VARIANTS["llama3-405b-layer-decode"])}
+
+
 # ----------------------------------------------------------------------------
 # raw draws
 # ----------------------------------------------------------------------------

@@ -304,7 +304,7 @@ def test_half_split_rope_bf16_prefill_and_decode():
 # ----------------------------------------------------------------------------
 
 def test_mqa_bf16_prefill_and_cache():
-    w = synth.scaled(W[3], num_key_value_heads=1, batch=2, seq_len=300)
+    w = synth.scaled(synth.VARIANTS["llama3-8b-mqa-layer-prefill"], batch=2, seq_len=300)
     got, ref, (layer, cache, sids, k_ref, v_ref) = _prefill_case(w, block_seed=6)
     e = P.assert_close(got, ref, "bf16", "MQA prefill")
     print("MQA prefill", e)
@@ -315,7 +315,7 @@ def test_mqa_bf16_prefill_and_cache():
 
 def test_mqa_decode_ragged_lengths_two_steps():
     # 32 query heads on one K/V head: two 16-head workgroups per key chunk
-    w = synth.scaled(W[4], num_key_value_heads=1, batch=5)
+    w = synth.scaled(synth.VARIANTS["llama3-8b-mqa-layer-decode"], batch=5)
     layer, cache, sids, host, wo = _decode_setup(w, lens=[1, 16, 333, 1024, 2049], block_seed=8)
     for step in range(2):
         xt = synth.decode_input(w, step)
@@ -345,8 +345,7 @@ def test_mqa_tiny_fp32_prefill_and_decode():
         P.assert_close(P.to_np(o), r, "f32", f"MQA fp32 decode step {step}")
 
 
-LLAMA3_405B = synth.scaled(W[5], hidden_size=16384, intermediate_size=53248, num_attention_heads=128,
-                           num_key_value_heads=8, batch=2, seq_len=300)
+LLAMA3_405B = synth.scaled(synth.VARIANTS["llama3-405b-layer-prefill"], batch=2, seq_len=300)
 
 
 def test_llama3_405b_layer_prefill_sampled_rows_and_decode():
