@@ -492,3 +492,100 @@ def test_swiglu_sizing_rule():
         d, I = g[name]["hidden"], g[name]["intermediate"]
         assert 3 * d * I / (8 * d * d) == pytest.approx(1.3125)
         assert g[name]["q_heads"] // g[name]["kv_heads"] == g[name]["ratio"]
+
+
+# ----------------------------------------------------------------------------
+# N-layer stack + final RMSNorm
+# ----------------------------------------------------------------------------
+
+def test_round_storage_bf16_known_values_and_ties():
+    from oracle.stack import round_storage
+    cases = [(1.0 + 2.0 ** -8, 1.0),                    # half-way, 1.0 is even
+             (1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -6),    # half-way, the upper neighbour is even
+             (1.0 + 2.0 ** -8 + 2.0 ** -30, 1.0 + 2.0 ** -7),  # just above half-way
+             (-(1.0 + 2.0 ** -8), -1.0),
+             (0.1, 0.10009765625),                     # 0x3DCD
+             (3.0, 3.0), (-2.0 ** -20, -2.0 ** -20), (0.0, 0.0)]
+    for v, want in cases:
+        assert round_storage(np.array([v]), "bf16")[0] == want, v
+
+
+def test_round_storage_bf16_matches_torch_rounding_of_float32():
+    import torch
+    from oracle.stack import round_storage
+    v = (rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))).astype(np.float32)
+    want = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(round_storage(v.astype(np.float64), "bf16"), want)
+
+
+def test_round_storage_f32_matches_struct_packing():
+    import struct
+    from oracle.stack import round_storage
+    v = rng.standard_normal(2000) * 3.0
+    want = np.array([struct.unpack("<f", struct.pack("<f", float(a)))[0] for a in v])
+    np.testing.assert_array_equal(round_storage(v, "f32"), want)
+
+
+def _stack_case(n_layers=3, H=4, G=2, d=16, I=12, gamma_std=0.2):
+    cfg = _tiny_cfg(H=H, G=G, d=d, I=I)
+    layers = [_tiny_weights(cfg, seed=100 + l) for l in range(n_layers)]
+    gf = 1.0 + gamma_std * rng.standard_normal(d)
+    return cfg, layers, gf
+
+
+def test_stack_with_zero_residual_branches_is_the_final_norm_of_its_input():
+    # o_proj = 0 and down_proj = 0 make every layer the identity on x
+    cfg, layers, gf = _stack_case()
+    for w in layers:
+        w["o_proj"] = np.zeros_like(w["o_proj"])
+        w["down_proj"] = np.zeros_like(w["down_proj"])
+    from oracle.stack import round_storage
+    x = round_storage(rng.standard_normal((2, 7, 16)), "bf16")
+    y, _, _ = oracle.stack_prefill(cfg, layers, gf, x, "bf16")
+    for b in range(2):
+        for t in range(7):
+            row = x[b, t]
+            r = 1.0 / math.sqrt(sum(v * v for v in row) / len(row) + cfg["rms_norm_eps"])
+            np.testing.assert_allclose(y[b, t], [row[i] * r * gf[i] for i in range(16)], rtol=1e-13, atol=1e-14)
+
+
+def test_stack_matches_scalar_brute_force_composition():
+    from oracle.stack import round_storage
+    cfg, layers, gf = _stack_case(n_layers=2, H=4, G=1)
+    x = round_storage(rng.standard_normal((5, 16)), "bf16")
+    h = x
+    for w in layers:
+        h = round_storage(_brute_layer(cfg, w, h), "bf16")
+    eps = cfg["rms_norm_eps"]
+    want = [[v / math.sqrt(sum(u * u for u in row) / len(row) + eps) * gf[i] for i, v in enumerate(row)]
+            for row in h.tolist()]
+    y, k, v = oracle.stack_prefill(cfg, layers, gf, x[None], "bf16")
+    np.testing.assert_allclose(y[0], want, rtol=1e-10, atol=1e-12)
+    assert k.shape == (2, 1, 5, 1, 4) and v.shape == (2, 1, 5, 1, 4)
+
+
+def test_stack_boundary_rounding_is_applied():
+    # without the rounding between layers the result moves by about 2^-9
+    from oracle.stack import round_storage
+    cfg, layers, gf = _stack_case(n_layers=2)
+    x = round_storage(rng.standard_normal((1, 6, 16)), "bf16")
+    y_bf, _, _ = oracle.stack_prefill(cfg, layers, gf, x, "bf16")
+    y_f32, _, _ = oracle.stack_prefill(cfg, layers, gf, x, "f32")
+    rel = np.abs(y_bf - y_f32).max() / np.abs(y_f32).max()
+    assert 1e-5 < rel < 2e-2
+
+
+def test_stack_decode_reproduces_full_recompute():
+    # a token decoded against the per-layer caches of a prefill gets the output
+    # the full prefill gives at its position ("Chapter 10", section 7)
+    from oracle.stack import round_storage
+    cfg, layers, gf = _stack_case(n_layers=3, H=4, G=2)
+    x = round_storage(rng.standard_normal((2, 9, 16)), "bf16")
+    full, _, _ = oracle.stack_prefill(cfg, layers, gf, x, "bf16")
+    part, k, v = oracle.stack_prefill(cfg, layers, gf, x[:, :7], "bf16")
+    np.testing.assert_allclose(part, full[:, :7], rtol=1e-12, atol=1e-13)
+    caches = [[(k[l, b], v[l, b]) for b in range(2)] for l in range(3)]
+    for t in (7, 8):
+        y, caches = oracle.stack_decode_step(cfg, layers, gf, x[:, t], caches, "bf16")
+        np.testing.assert_allclose(y, full[:, t], rtol=1e-10, atol=1e-12)
+    assert caches[2][1][0].shape == (9, 2, 4)
