@@ -83,6 +83,11 @@ hipError_t launch_rms_rowscale(DType t, const void* x, float* r, void* xt, int M
 hipError_t launch_rms_convert(DType t, const float* h, const float* gamma, void* hb, float* r,
                               int M, int d, float eps, hipStream_t s);
 
+// Final RMSNorm of a layer stack: y [M][d] (out_t, row-major) = x * rsqrt(mean(x^2)
+// + eps) * gamma, x [M][d] and gamma [d] in the layer dtype t.
+hipError_t launch_rms_norm_out(DType t, const void* x, const void* gamma, void* y, DType out_t, int M, int d,
+                               float eps, hipStream_t s);
+
 // Causal GQA prefill attention: q [B*S][H*D] -> attn [B*S][H*D] (bf16 tiled),
 // keys from the cache.
 hipError_t launch_attn_prefill(DType t, const void* q, void* attn, int H, const CacheView& c,

@@ -191,10 +191,14 @@ bool trace_on() {
 // ---------------------------------------------------------------------------
 
 namespace {
-enum Kern { K_RMS1, K_QKV, K_ATTN_PREFILL, K_ATTN_DECODE, K_ATTN_COMBINE, K_OPROJ, K_RMS2, K_GATEUP, K_DOWN, K_COUNT };
+enum Kern {
+  K_RMS1, K_QKV, K_ATTN_PREFILL, K_ATTN_DECODE, K_ATTN_COMBINE, K_OPROJ, K_RMS2, K_GATEUP, K_DOWN, K_FINAL_NORM,
+  K_COUNT
+};
 const char* const kKernNames[K_COUNT] = {"rms_rowscale",   "gemm_qkv_rope",     "attn_prefill",
                                          "attn_decode_split", "attn_decode_combine", "gemm_o_resid",
-                                         "rms_convert",    "gemm_gate_up_swiglu", "gemm_down_resid"};
+                                         "rms_convert",    "gemm_gate_up_swiglu", "gemm_down_resid",
+                                         "rms_final_norm"};
 struct Pending {
   int kind;
   void* start;
@@ -264,6 +268,8 @@ struct SeqState {
 struct llama_kv_cache {
   Shape s;
   int num_blocks, max_seqs, max_blocks;
+  int n_layers;        // layers sharing the block tables; pools are [n_layers][num_blocks] blocks
+  size_t layer_bytes;  // bytes of one layer's K (or V) pool
   void* k_pool;
   void* v_pool;
   int32_t* table;
@@ -278,24 +284,26 @@ size_t pool_bytes(const Shape& s, int num_blocks) { return (size_t)num_blocks * 
 struct CacheLayout {
   size_t k, v, table, total;
 };
-CacheLayout cache_layout(const Shape& s, int num_blocks, int max_seqs) {
+CacheLayout cache_layout(const Shape& s, int num_blocks, int max_seqs, int n_layers) {
   CacheLayout c;
   const int max_blocks = (s.max_pos + kBlock - 1) / kBlock;
   size_t off = 0;
   c.k = off;
-  off = align256(off + pool_bytes(s, num_blocks));
+  off = align256(off + (size_t)n_layers * pool_bytes(s, num_blocks));
   c.v = off;
-  off = align256(off + pool_bytes(s, num_blocks));
+  off = align256(off + (size_t)n_layers * pool_bytes(s, num_blocks));
   c.table = off;
   off = align256(off + (size_t)max_seqs * max_blocks * sizeof(int32_t));
   c.total = off;
   return c;
 }
 
-llk::CacheView cache_view(const llama_kv_cache* c) {
+// The cache as the kernels of layer `layer` see it: that layer's pools, the
+// shared block tables.
+llk::CacheView cache_view(const llama_kv_cache* c, int layer = 0) {
   llk::CacheView v;
-  v.k_pool = c->k_pool;
-  v.v_pool = c->v_pool;
+  v.k_pool = reinterpret_cast<char*>(c->k_pool) + (size_t)layer * c->layer_bytes;
+  v.v_pool = reinterpret_cast<char*>(c->v_pool) + (size_t)layer * c->layer_bytes;
   v.block_table = c->table;
   v.max_blocks = c->max_blocks;
   v.G = c->s.G;
@@ -537,21 +545,26 @@ llama_status llama_layer_profile_read(llama_layer* layer, llama_kernel_time* out
 
 // ---- cache ----------------------------------------------------------------
 
-llama_status llama_kv_cache_bytes(const llama_layer_config* cfg, int32_t num_blocks, int32_t block_size,
-                                  int32_t max_seqs, size_t* bytes) {
-  if (!bytes || num_blocks <= 0 || max_seqs <= 0) return LLAMA_ERR_INVALID_ARG;
+llama_status llama_kv_cache_bytes_layers(const llama_layer_config* cfg, int32_t n_layers, int32_t num_blocks,
+                                         int32_t block_size, int32_t max_seqs, size_t* bytes) {
+  if (!bytes || n_layers <= 0 || num_blocks <= 0 || max_seqs <= 0) return LLAMA_ERR_INVALID_ARG;
   Shape s;
   llama_status st = check_config(cfg, &s);
   if (st != LLAMA_OK) return st;
   if (block_size != kBlock) return LLAMA_ERR_UNSUPPORTED;
-  *bytes = cache_layout(s, num_blocks, max_seqs).total;
+  *bytes = cache_layout(s, num_blocks, max_seqs, n_layers).total;
   return LLAMA_OK;
 }
 
-llama_status llama_kv_cache_create(const llama_layer_config* cfg, int32_t num_blocks, int32_t block_size,
-                                   int32_t max_seqs, const int32_t* block_order, void* pool_dev,
-                                   llama_kv_cache** out) {
-  if (!out || !pool_dev || num_blocks <= 0 || max_seqs <= 0) return LLAMA_ERR_INVALID_ARG;
+llama_status llama_kv_cache_bytes(const llama_layer_config* cfg, int32_t num_blocks, int32_t block_size,
+                                  int32_t max_seqs, size_t* bytes) {
+  return llama_kv_cache_bytes_layers(cfg, 1, num_blocks, block_size, max_seqs, bytes);
+}
+
+llama_status llama_kv_cache_create_layers(const llama_layer_config* cfg, int32_t n_layers, int32_t num_blocks,
+                                          int32_t block_size, int32_t max_seqs, const int32_t* block_order,
+                                          void* pool_dev, llama_kv_cache** out) {
+  if (!out || !pool_dev || n_layers <= 0 || num_blocks <= 0 || max_seqs <= 0) return LLAMA_ERR_INVALID_ARG;
   if (!aligned(pool_dev, 256)) return LLAMA_ERR_INVALID_ARG;
   Shape s;
   llama_status st = check_config(cfg, &s);
@@ -571,17 +584,31 @@ llama_status llama_kv_cache_create(const llama_layer_config* cfg, int32_t num_bl
   }
   llama_kv_cache* c = new (std::nothrow) llama_kv_cache;
   if (!c) return LLAMA_ERR_INVALID_ARG;
-  const CacheLayout cl = cache_layout(s, num_blocks, max_seqs);
+  const CacheLayout cl = cache_layout(s, num_blocks, max_seqs, n_layers);
   c->s = s;
   c->num_blocks = num_blocks;
   c->max_seqs = max_seqs;
   c->max_blocks = (s.max_pos + kBlock - 1) / kBlock;
+  c->n_layers = n_layers;
+  c->layer_bytes = pool_bytes(s, num_blocks);
   c->k_pool = reinterpret_cast<char*>(pool_dev) + cl.k;
   c->v_pool = reinterpret_cast<char*>(pool_dev) + cl.v;
   c->table = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(pool_dev) + cl.table);
   c->free_blocks.assign(order.rbegin(), order.rend());
   c->seqs.resize(max_seqs);
   *out = c;
+  return LLAMA_OK;
+}
+
+llama_status llama_kv_cache_create(const llama_layer_config* cfg, int32_t num_blocks, int32_t block_size,
+                                   int32_t max_seqs, const int32_t* block_order, void* pool_dev,
+                                   llama_kv_cache** out) {
+  return llama_kv_cache_create_layers(cfg, 1, num_blocks, block_size, max_seqs, block_order, pool_dev, out);
+}
+
+llama_status llama_kv_cache_num_layers(const llama_kv_cache* c, int32_t* n) {
+  if (!c || !n) return LLAMA_ERR_INVALID_ARG;
+  *n = c->n_layers;
   return LLAMA_OK;
 }
 
@@ -636,8 +663,11 @@ llama_status llama_kv_cache_write(llama_kv_cache* c, int32_t seq_id, int32_t n_t
   if (st != LLAMA_OK) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   HIP_TRY(up.flush(hs));
-  HIP_TRY(llk::launch_kv_copy(c->s.dt, cache_view(c), seq_id, start, n_tokens, const_cast<void*>(k_dev),
-                              const_cast<void*>(v_dev), true, hs));
+  const size_t per_layer = (size_t)n_tokens * c->s.KD * c->s.es;  // bytes of one layer's [n, G, D]
+  for (int l = 0; l < c->n_layers; ++l)
+    HIP_TRY(llk::launch_kv_copy(c->s.dt, cache_view(c, l), seq_id, start, n_tokens,
+                                const_cast<char*>(reinterpret_cast<const char*>(k_dev)) + l * per_layer,
+                                const_cast<char*>(reinterpret_cast<const char*>(v_dev)) + l * per_layer, true, hs));
   c->seqs[seq_id].len += n_tokens;
   return LLAMA_OK;
 }
@@ -647,47 +677,63 @@ llama_status llama_kv_cache_read(const llama_kv_cache* c, int32_t seq_id, int32_
   if (!c || !k_dev || !v_dev || n <= 0 || start < 0) return LLAMA_ERR_INVALID_ARG;
   if (seq_id < 0 || seq_id >= c->max_seqs || !c->seqs[seq_id].open) return LLAMA_ERR_BAD_SEQ;
   if ((long)start + n > c->seqs[seq_id].len) return LLAMA_ERR_POSITION;
-  HIP_TRY(llk::launch_kv_copy(c->s.dt, cache_view(c), seq_id, start, n, k_dev, v_dev, false,
-                              reinterpret_cast<hipStream_t>(stream)));
+  const size_t per_layer = (size_t)n * c->s.KD * c->s.es;
+  for (int l = 0; l < c->n_layers; ++l)
+    HIP_TRY(llk::launch_kv_copy(c->s.dt, cache_view(c, l), seq_id, start, n,
+                                reinterpret_cast<char*>(k_dev) + l * per_layer,
+                                reinterpret_cast<char*>(v_dev) + l * per_layer, false,
+                                reinterpret_cast<hipStream_t>(stream)));
   return LLAMA_OK;
 }
 
 // ---- forward ----------------------------------------------------------------
 
-static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, int32_t seq_len,
-                            const int32_t* seq_ids, const void* x, void* out, int32_t out_dtype, void* workspace,
-                            void* stream, bool decode) {
-  if (!L || !c || !seq_ids || !x || !out || !workspace) return LLAMA_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+// Argument checks common to a layer call and a stack call.
+llama_status check_call(const Shape& s, const llama_kv_cache* c, int32_t batch, int32_t seq_len,
+                        const int32_t* seq_ids, const void* x, const void* out, int32_t out_dtype,
+                        const void* workspace) {
+  if (!c || !seq_ids || !x || !out || !workspace) return LLAMA_ERR_INVALID_ARG;
   if (batch <= 0 || seq_len <= 0) return LLAMA_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(out, 16) || !aligned(workspace, 256)) return LLAMA_ERR_INVALID_ARG;
   if (out_dtype != LLAMA_DTYPE_F32 && out_dtype != LLAMA_DTYPE_BF16) return LLAMA_ERR_DTYPE;
-  if (L->s.dt == DType::F32 && out_dtype != LLAMA_DTYPE_F32) return LLAMA_ERR_DTYPE;
-  if (!same_shape(L->s, c->s)) return LLAMA_ERR_SHAPE;
-  const long T = (long)batch * seq_len;
-  if (T > (1L << 24)) return LLAMA_ERR_SHAPE;
-  const Shape& s = L->s;
+  if (s.dt == DType::F32 && out_dtype != LLAMA_DTYPE_F32) return LLAMA_ERR_DTYPE;
+  if (!same_shape(s, c->s)) return LLAMA_ERR_SHAPE;
+  if ((long)batch * seq_len > (1L << 24)) return LLAMA_ERR_SHAPE;
+  return LLAMA_OK;
+}
 
+// Host bookkeeping of one call, shared by every layer it runs: reserve the
+// sequences' new blocks, queue the block-table and batch-descriptor stores
+// (all but the last batch of them launched here; the last rides on the first
+// kernel), and advance the sequence lengths.
+llama_status begin_call(llama_kv_cache* c, int32_t batch, int32_t seq_len, const int32_t* seq_ids, int32_t* desc,
+                        hipStream_t hs, const llk::Upload** last_upload, Uploader* up) {
   std::vector<int32_t> start(batch);
   for (int b = 0; b < batch; ++b)
     start[b] = (seq_ids[b] >= 0 && seq_ids[b] < c->max_seqs) ? c->seqs[seq_ids[b]].len : 0;
-  Uploader up;
-  llama_status st = reserve(c, batch, seq_ids, seq_len, &up);
+  llama_status st = reserve(c, batch, seq_ids, seq_len, up);
   if (st != LLAMA_OK) return st;
-
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  const WsLayout wl = ws_layout(s, (size_t)T, (size_t)batch);
-  char* W = reinterpret_cast<char*>(workspace);
-  int32_t* desc = reinterpret_cast<int32_t*>(W + wl.desc);
   for (int b = 0; b < batch; ++b) {
-    up.add(desc, 2 * b, seq_ids[b]);
-    up.add(desc, 2 * b + 1, start[b]);
+    up->add(desc, 2 * b, seq_ids[b]);
+    up->add(desc, 2 * b + 1, start[b]);
   }
   // lengths are committed now: every later failure is a device failure
   for (int b = 0; b < batch; ++b) c->seqs[seq_ids[b]].len += seq_len;
-  // the last upload batch rides on the first norm kernel's launch
-  const llk::Upload* last_upload = nullptr;
-  HIP_TRY(up.flush_all_but_last(hs, &last_upload));
+  HIP_TRY(up->flush_all_but_last(hs, last_upload));
+  return LLAMA_OK;
+}
 
+// The kernels of one layer over the tokens of a call (begin_call done):
+// x [M][d] in the layer dtype -> out [M][d] in out_t; K/V of the new tokens
+// go to the pools of `cv`.
+llama_status run_layer(llama_layer* L, const llk::CacheView& cv, const llk::BatchView& bv, int M, const void* x,
+                       void* out, DType out_t, char* W, const WsLayout& wl, const llk::Upload* last_upload,
+                       hipStream_t hs, bool decode) {
+  const Shape& s = L->s;
   float* r1 = reinterpret_cast<float*>(W + wl.r1);
   float* r2 = reinterpret_cast<float*>(W + wl.r2);
   void* xt = s.dt == DType::BF16 ? W + wl.xt : nullptr;  // tiled copy of x (QKV operand)
@@ -699,10 +745,6 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
   float* part = reinterpret_cast<float*>(W + wl.part);
   const char* P = L->packed;
   const float eps = L->cfg.rms_norm_eps;
-  const int M = (int)T;
-
-  llk::BatchView bv{desc, batch, seq_len};
-  llk::CacheView cv = cache_view(c);
   float* gpart = reinterpret_cast<float*>(W + wl.gpart);
   auto tile_for = [&](int N) {
     if (use_skinny(s, M)) return llk::GemmTile::SKINNY;
@@ -711,7 +753,7 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
   };
   if (trace_on())
     std::fprintf(stderr, "[llama_layer] %s B=%d S=%d T=%d d=%d H=%d G=%d D=%d I=%d\n", decode ? "decode" : "prefill",
-                 batch, seq_len, M, s.d, s.H, s.G, s.D, s.I);
+                 bv.batch, bv.seq_len, M, s.d, s.H, s.G, s.D, s.I);
 
   // RMSNorm_1 statistics
   HIP_TRY(timed(L, K_RMS1, hs,
@@ -798,9 +840,151 @@ static llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, in
   dn.resid = h;
   dn.out = out;
   dn.ldo = s.d;
-  dn.out_dtype = out_dtype == LLAMA_DTYPE_F32 ? DType::F32 : DType::BF16;
+  dn.out_dtype = out_t;
   HIP_TRY(timed(L, K_DOWN, hs, [&] { return llk::launch_gemm(s.dt, tile_for(dn.N), dn, hs); }));
   return LLAMA_OK;
+}
+
+llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, int32_t seq_len, const int32_t* seq_ids,
+                     const void* x, void* out, int32_t out_dtype, void* workspace, void* stream, bool decode) {
+  if (!L) return LLAMA_ERR_INVALID_ARG;
+  llama_status st = check_call(L->s, c, batch, seq_len, seq_ids, x, out, out_dtype, workspace);
+  if (st != LLAMA_OK) return st;
+  if (c->n_layers != 1) return LLAMA_ERR_SHAPE;  // a multi-layer cache belongs to a stack
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const int M = batch * seq_len;
+  const WsLayout wl = ws_layout(L->s, (size_t)M, (size_t)batch);
+  char* W = reinterpret_cast<char*>(workspace);
+  int32_t* desc = reinterpret_cast<int32_t*>(W + wl.desc);
+  Uploader up;
+  const llk::Upload* last_upload = nullptr;
+  st = begin_call(c, batch, seq_len, seq_ids, desc, hs, &last_upload, &up);
+  if (st != LLAMA_OK) return st;
+  const llk::BatchView bv{desc, batch, seq_len};
+  return run_layer(L, cache_view(c), bv, M, x, out, out_dtype == LLAMA_DTYPE_F32 ? DType::F32 : DType::BF16, W, wl,
+                   last_upload, hs, decode);
+}
+
+}  // namespace
+
+extern "C" {
+
+// ---- stack ------------------------------------------------------------------
+
+}  // extern "C"
+
+struct llama_stack {
+  std::vector<llama_layer*> layers;
+  const void* final_norm;  // [d] in the layer dtype, caller-owned
+};
+
+namespace {
+
+bool same_config(const llama_layer_config& a, const llama_layer_config& b) {
+  return a.hidden_size == b.hidden_size && a.intermediate_size == b.intermediate_size &&
+         a.num_attention_heads == b.num_attention_heads && a.num_key_value_heads == b.num_key_value_heads &&
+         a.rms_norm_eps == b.rms_norm_eps && a.rope_theta == b.rope_theta && a.max_position == b.max_position &&
+         a.dtype == b.dtype && a.rope_style == b.rope_style;
+}
+
+// Workspace of a stack call: one layer's workspace (reused by every layer in
+// turn), then two [T][d] hidden-state buffers in the layer dtype that the
+// layers write in alternation.
+struct StackWs {
+  WsLayout layer;
+  size_t act[2], total;
+};
+StackWs stack_ws(const Shape& s, size_t T, size_t B) {
+  StackWs w;
+  w.layer = ws_layout(s, T, B);
+  size_t off = w.layer.total;
+  for (int i = 0; i < 2; ++i) {
+    w.act[i] = off;
+    off = align256(off + T * s.d * s.es);
+  }
+  w.total = off;
+  return w;
+}
+
+llama_status stack_forward(llama_stack* S, llama_kv_cache* c, int32_t batch, int32_t seq_len,
+                           const int32_t* seq_ids, const void* x, void* out, int32_t out_dtype, void* workspace,
+                           void* stream, bool decode) {
+  if (!S) return LLAMA_ERR_INVALID_ARG;
+  llama_layer* L0 = S->layers[0];
+  llama_status st = check_call(L0->s, c, batch, seq_len, seq_ids, x, out, out_dtype, workspace);
+  if (st != LLAMA_OK) return st;
+  const int nl = (int)S->layers.size();
+  if (c->n_layers != nl) return LLAMA_ERR_SHAPE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  const int M = batch * seq_len;
+  const StackWs sw = stack_ws(L0->s, (size_t)M, (size_t)batch);
+  char* W = reinterpret_cast<char*>(workspace);
+  int32_t* desc = reinterpret_cast<int32_t*>(W + sw.layer.desc);
+  Uploader up;
+  const llk::Upload* last_upload = nullptr;
+  st = begin_call(c, batch, seq_len, seq_ids, desc, hs, &last_upload, &up);
+  if (st != LLAMA_OK) return st;
+  const llk::BatchView bv{desc, batch, seq_len};
+  // x_{l+1} = layer_l(x_l), held in the layer dtype between layers
+  const void* cur = x;
+  for (int l = 0; l < nl; ++l) {
+    void* nxt = W + sw.act[l & 1];
+    st = run_layer(S->layers[l], cache_view(c, l), bv, M, cur, nxt, L0->s.dt, W, sw.layer,
+                   l == 0 ? last_upload : nullptr, hs, decode);
+    if (st != LLAMA_OK) return st;
+    cur = nxt;
+  }
+  // y = RMSNorm_final(x_L), timed with the last layer's kernels
+  llama_layer* Ll = S->layers[nl - 1];
+  const DType out_t = out_dtype == LLAMA_DTYPE_F32 ? DType::F32 : DType::BF16;
+  HIP_TRY(timed(Ll, K_FINAL_NORM, hs, [&] {
+    return llk::launch_rms_norm_out(L0->s.dt, cur, S->final_norm, out, out_t, M, L0->s.d, L0->cfg.rms_norm_eps, hs);
+  }));
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+llama_status llama_stack_create(llama_layer* const* layers, int32_t n_layers, const void* final_norm,
+                                llama_stack** out) {
+  if (!layers || n_layers <= 0 || !final_norm || !out) return LLAMA_ERR_INVALID_ARG;
+  if (!aligned(final_norm, 16)) return LLAMA_ERR_INVALID_ARG;
+  for (int l = 0; l < n_layers; ++l) {
+    if (!layers[l]) return LLAMA_ERR_INVALID_ARG;
+    if (!same_config(layers[l]->cfg, layers[0]->cfg)) return LLAMA_ERR_SHAPE;
+  }
+  llama_stack* S = new (std::nothrow) llama_stack;
+  if (!S) return LLAMA_ERR_INVALID_ARG;
+  S->layers.assign(layers, layers + n_layers);
+  S->final_norm = final_norm;
+  *out = S;
+  return LLAMA_OK;
+}
+
+llama_status llama_stack_workspace_bytes(const llama_stack* S, int32_t max_tokens, int32_t max_batch,
+                                         size_t* bytes) {
+  if (!S || !bytes || max_tokens <= 0 || max_batch <= 0 || max_batch > max_tokens) return LLAMA_ERR_INVALID_ARG;
+  *bytes = stack_ws(S->layers[0]->s, (size_t)max_tokens, (size_t)max_batch).total;
+  return LLAMA_OK;
+}
+
+llama_status llama_stack_destroy(llama_stack* S) {
+  if (!S) return LLAMA_ERR_INVALID_ARG;
+  delete S;
+  return LLAMA_OK;
+}
+
+llama_status llama_stack_prefill(llama_stack* stack, llama_kv_cache* cache, int32_t batch, int32_t seq_len,
+                                 const int32_t* seq_ids, const void* x, void* out, int32_t out_dtype,
+                                 void* workspace, void* stream) {
+  return stack_forward(stack, cache, batch, seq_len, seq_ids, x, out, out_dtype, workspace, stream, false);
+}
+
+llama_status llama_stack_decode(llama_stack* stack, llama_kv_cache* cache, int32_t batch, const int32_t* seq_ids,
+                                const void* x, void* out, int32_t out_dtype, void* workspace, void* stream) {
+  return stack_forward(stack, cache, batch, 1, seq_ids, x, out, out_dtype, workspace, stream, true);
 }
 
 llama_status llama_layer_prefill(llama_layer* layer, llama_kv_cache* cache, int32_t batch, int32_t seq_len,

@@ -72,7 +72,71 @@ __global__ __launch_bounds__(256) void rms_convert_kernel(const float* __restric
   if (lane == 0) r[row] = 1.f / sqrtf(acc / (float)d + eps);
 }
 
+// Final RMSNorm of a stack of layers: y = x * rsqrt(mean(x^2) + eps) * gamma
+// ("From Transformer to the LLaMA series", sections 3.3 and 8: the norm after
+// the last block), x and gamma in the layer dtype, y row-major in the output
+// dtype.  One wavefront per row: the statistics pass reads the row from HBM,
+// the scaling pass reads it again while it is still in the L2.
+template <typename T, typename TO>
+__global__ __launch_bounds__(256) void rms_norm_out_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
+                                                           TO* __restrict__ y, int M, int d, float eps) {
+  constexpr int N = Chunk<T>::N;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const T* p = x + (size_t)row * d;
+  float acc = 0.f;
+#pragma unroll 8
+  for (int c = lane * N; c < d; c += 64 * N) {
+    const auto v = load_chunk<T>(p + c);
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      const float f = to_f32(v[e]);
+      acc += f * f;
+    }
+  }
+  acc = wave_sum(acc);
+  const float r = 1.f / sqrtf(acc / (float)d + eps);
+  TO* q = y + (size_t)row * d;
+#pragma unroll 4
+  for (int c = lane * N; c < d; c += 64 * N) {
+    const auto v = load_chunk<T>(p + c);
+    const auto g = load_chunk<T>(gamma + c);
+    float f[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e) f[e] = to_f32(v[e]) * r * to_f32(g[e]);
+#pragma unroll
+    for (int e = 0; e < N; e += 4) {
+      if constexpr (sizeof(TO) == 4)
+        *reinterpret_cast<f32x4*>(q + c + e) = f32x4{f[e], f[e + 1], f[e + 2], f[e + 3]};
+      else
+        *reinterpret_cast<bf16x4*>(q + c + e) =
+            bf16x4{from_f32<bf16>(f[e]), from_f32<bf16>(f[e + 1]), from_f32<bf16>(f[e + 2]), from_f32<bf16>(f[e + 3])};
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_rms_norm_out(DType t, const void* x, const void* gamma, void* y, DType out_t, int M, int d,
+                               float eps, hipStream_t s) {
+  const int grid = (M + 3) / 4;
+  if (M <= 0 || d % 8 != 0) return hipErrorInvalidValue;
+  if (t == DType::BF16) {
+    const bf16* xb = reinterpret_cast<const bf16*>(x);
+    const bf16* gb = reinterpret_cast<const bf16*>(gamma);
+    if (out_t == DType::BF16)
+      rms_norm_out_kernel<bf16, bf16><<<grid, 256, 0, s>>>(xb, gb, reinterpret_cast<bf16*>(y), M, d, eps);
+    else
+      rms_norm_out_kernel<bf16, float><<<grid, 256, 0, s>>>(xb, gb, reinterpret_cast<float*>(y), M, d, eps);
+  } else {
+    if (out_t != DType::F32) return hipErrorInvalidValue;
+    rms_norm_out_kernel<float, float><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(x),
+                                                           reinterpret_cast<const float*>(gamma),
+                                                           reinterpret_cast<float*>(y), M, d, eps);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_rms_rowscale(DType t, const void* x, float* r, void* xt, int M, int d, float eps,
                                const Upload* up, hipStream_t s) {

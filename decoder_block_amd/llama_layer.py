@@ -30,7 +30,9 @@ EXPORTED = ("llama_status_string", "llama_layer_packed_bytes", "llama_layer_crea
             "llama_kv_cache_create", "llama_kv_cache_destroy", "llama_kv_cache_add_seq",
             "llama_kv_cache_free_seq", "llama_kv_cache_seq_len", "llama_kv_cache_free_blocks",
             "llama_kv_cache_write", "llama_kv_cache_read", "llama_layer_prefill", "llama_layer_decode",
-            "llama_layer_profile_enable", "llama_layer_profile_read")
+            "llama_layer_profile_enable", "llama_layer_profile_read", "llama_kv_cache_bytes_layers",
+            "llama_kv_cache_create_layers", "llama_kv_cache_num_layers", "llama_stack_create",
+            "llama_stack_workspace_bytes", "llama_stack_destroy", "llama_stack_prefill", "llama_stack_decode")
 
 
 class LlamaError(RuntimeError):
@@ -88,6 +90,15 @@ def lib() -> ctypes.CDLL:
         "llama_layer_decode": (ctypes.c_int, [P, P, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, P]),
         "llama_layer_profile_enable": (ctypes.c_int, [P, I32]),
         "llama_layer_profile_read": (ctypes.c_int, [P, ctypes.POINTER(LlamaKernelTime), I32, ctypes.POINTER(I32), I32]),
+        "llama_kv_cache_bytes_layers": (ctypes.c_int, [cfgp, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
+        "llama_kv_cache_create_layers": (ctypes.c_int, [cfgp, I32, I32, I32, I32, ctypes.POINTER(I32), P,
+                                                        ctypes.POINTER(P)]),
+        "llama_kv_cache_num_layers": (ctypes.c_int, [P, ctypes.POINTER(I32)]),
+        "llama_stack_create": (ctypes.c_int, [ctypes.POINTER(P), I32, P, ctypes.POINTER(P)]),
+        "llama_stack_workspace_bytes": (ctypes.c_int, [P, I32, I32, ctypes.POINTER(SZ)]),
+        "llama_stack_destroy": (ctypes.c_int, [P]),
+        "llama_stack_prefill": (ctypes.c_int, [P, P, I32, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, P]),
+        "llama_stack_decode": (ctypes.c_int, [P, P, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -175,6 +186,58 @@ def llama_kv_cache_create(cfg: LlamaLayerConfig, num_blocks: int, block_size: in
     _check(lib().llama_kv_cache_create(ctypes.byref(cfg), num_blocks, block_size, max_seqs, order,
                                        _ptr(pool_dev), ctypes.byref(h)), "llama_kv_cache_create")
     return h
+
+
+def llama_kv_cache_bytes_layers(cfg: LlamaLayerConfig, n_layers: int, num_blocks: int, block_size: int,
+                                max_seqs: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().llama_kv_cache_bytes_layers(ctypes.byref(cfg), n_layers, num_blocks, block_size, max_seqs,
+                                             ctypes.byref(n)), "llama_kv_cache_bytes_layers")
+    return n.value
+
+
+def llama_kv_cache_create_layers(cfg: LlamaLayerConfig, n_layers: int, num_blocks: int, block_size: int,
+                                 max_seqs: int, pool_dev, block_order=None):
+    h = ctypes.c_void_p()
+    order = _i32_array(block_order) if block_order is not None else None
+    _check(lib().llama_kv_cache_create_layers(ctypes.byref(cfg), n_layers, num_blocks, block_size, max_seqs, order,
+                                              _ptr(pool_dev), ctypes.byref(h)), "llama_kv_cache_create_layers")
+    return h
+
+
+def llama_kv_cache_num_layers(cache) -> int:
+    n = ctypes.c_int32()
+    _check(lib().llama_kv_cache_num_layers(cache, ctypes.byref(n)), "llama_kv_cache_num_layers")
+    return n.value
+
+
+def llama_stack_create(layers, final_norm):
+    h = ctypes.c_void_p()
+    arr = (ctypes.c_void_p * len(layers))(*[l.value if isinstance(l, ctypes.c_void_p) else l for l in layers])
+    _check(lib().llama_stack_create(arr, len(layers), _ptr(final_norm), ctypes.byref(h)), "llama_stack_create")
+    return h
+
+
+def llama_stack_workspace_bytes(stack, max_tokens: int, max_batch: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().llama_stack_workspace_bytes(stack, max_tokens, max_batch, ctypes.byref(n)),
+           "llama_stack_workspace_bytes")
+    return n.value
+
+
+def llama_stack_destroy(stack):
+    _check(lib().llama_stack_destroy(stack), "llama_stack_destroy")
+
+
+def llama_stack_prefill(stack, cache, batch: int, seq_len: int, seq_ids, x, out, out_dtype: int,
+                        workspace, stream=None):
+    _check(lib().llama_stack_prefill(stack, cache, batch, seq_len, _i32_array(seq_ids), _ptr(x), _ptr(out),
+                                     out_dtype, _ptr(workspace), _stream(stream)), "llama_stack_prefill")
+
+
+def llama_stack_decode(stack, cache, batch: int, seq_ids, x, out, out_dtype: int, workspace, stream=None):
+    _check(lib().llama_stack_decode(stack, cache, batch, _i32_array(seq_ids), _ptr(x), _ptr(out), out_dtype,
+                                    _ptr(workspace), _stream(stream)), "llama_stack_decode")
 
 
 def llama_kv_cache_destroy(cache):
@@ -308,12 +371,16 @@ class DecoderLayer:
 
 
 class PagedKVCache:
-    """A paged K/V pool of ``num_blocks`` 16-token blocks for one layer."""
+    """A paged K/V pool of ``num_blocks`` 16-token blocks, for one layer or
+    (``n_layers`` > 1) for every layer of a stack, sharing one block table."""
 
-    def __init__(self, layer: DecoderLayer, num_blocks: int, max_seqs: int, block_order=None):
+    def __init__(self, layer: DecoderLayer, num_blocks: int, max_seqs: int, block_order=None, n_layers: int = 1):
         self.layer = layer
-        self.pool = _dev_bytes(llama_kv_cache_bytes(layer.cfg, num_blocks, 16, max_seqs), layer.device)
-        self.handle = llama_kv_cache_create(layer.cfg, num_blocks, 16, max_seqs, self.pool, block_order)
+        self.n_layers = n_layers
+        self.pool = _dev_bytes(llama_kv_cache_bytes_layers(layer.cfg, n_layers, num_blocks, 16, max_seqs),
+                               layer.device)
+        self.handle = llama_kv_cache_create_layers(layer.cfg, n_layers, num_blocks, 16, max_seqs, self.pool,
+                                                   block_order)
 
     def add_seq(self) -> int:
         return llama_kv_cache_add_seq(self.handle)
@@ -328,11 +395,15 @@ class PagedKVCache:
         return llama_kv_cache_free_blocks(self.handle)
 
     def write(self, sid: int, k: torch.Tensor, v: torch.Tensor, stream=None):
-        llama_kv_cache_write(self.handle, sid, k.shape[0], k, v, stream)
+        """k, v: [n, G, D] (one layer) or [n_layers, n, G, D]."""
+        n = k.shape[0] if self.n_layers == 1 and k.dim() == 3 else k.shape[1]
+        llama_kv_cache_write(self.handle, sid, n, k.contiguous(), v.contiguous(), stream)
 
     def read(self, sid: int, start: int, n: int):
+        """[n, G, D] K and V (one layer) or [n_layers, n, G, D]."""
         G, D = self.layer.cfg.num_key_value_heads, self.layer.cfg.hidden_size // self.layer.cfg.num_attention_heads
-        k = torch.empty((n, G, D), dtype=self.layer.tdtype, device=self.layer.device)
+        shape = (n, G, D) if self.n_layers == 1 else (self.n_layers, n, G, D)
+        k = torch.empty(shape, dtype=self.layer.tdtype, device=self.layer.device)
         v = torch.empty_like(k)
         llama_kv_cache_read(self.handle, sid, start, n, k, v)
         return k, v
@@ -340,6 +411,57 @@ class PagedKVCache:
     def close(self):
         if getattr(self, "handle", None):
             llama_kv_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class DecoderStack:
+    """``layers`` (DecoderLayer, one config) run in order, then the final RMSNorm
+    with gamma ``final_norm`` [d]; calls take a PagedKVCache with as many layers."""
+
+    def __init__(self, layers, final_norm: torch.Tensor):
+        self.layers = list(layers)
+        l0 = self.layers[0]
+        self.device = l0.device
+        self.final_norm = final_norm.to(l0.device, l0.tdtype).contiguous()
+        self.handle = llama_stack_create([l.handle for l in self.layers], self.final_norm)
+        self._ws = None
+
+    def cache(self, num_blocks: int, max_seqs: int, block_order=None) -> PagedKVCache:
+        return PagedKVCache(self.layers[0], num_blocks, max_seqs, block_order, n_layers=len(self.layers))
+
+    def workspace(self, tokens: int, batch: int) -> torch.Tensor:
+        need = llama_stack_workspace_bytes(self.handle, tokens, batch)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = _dev_bytes(need, self.device)
+        return self._ws
+
+    def prefill(self, cache: PagedKVCache, seq_ids, x: torch.Tensor, out_dtype="f32", out=None, stream=None):
+        B, S, d = x.shape
+        if out is None:
+            out = torch.empty((B, S, d), dtype=_TORCH_DT[out_dtype], device=self.device)
+        ws = self.workspace(B * S, B)
+        llama_stack_prefill(self.handle, cache.handle, B, S, list(seq_ids), x, out,
+                            LLAMA_DTYPE_F32 if out_dtype == "f32" else LLAMA_DTYPE_BF16, ws, stream)
+        return out
+
+    def decode(self, cache: PagedKVCache, seq_ids, x: torch.Tensor, out_dtype="f32", out=None, stream=None):
+        B, d = x.shape
+        if out is None:
+            out = torch.empty((B, d), dtype=_TORCH_DT[out_dtype], device=self.device)
+        ws = self.workspace(B, B)
+        llama_stack_decode(self.handle, cache.handle, B, list(seq_ids), x, out,
+                           LLAMA_DTYPE_F32 if out_dtype == "f32" else LLAMA_DTYPE_BF16, ws, stream)
+        return out
+
+    def close(self):
+        if getattr(self, "handle", None):
+            llama_stack_destroy(self.handle)
             self.handle = None
 
     def __del__(self):

@@ -183,20 +183,30 @@ def weight_shapes(w: Workload) -> dict:
             "input_layernorm": (d,), "post_attention_layernorm": (d,)}
 
 
-def layer_weights(w: Workload, gamma_std: float | None = None) -> dict:
-    """All nine parameter tensors in storage dtype (CPU)."""
+def layer_weights(w: Workload, gamma_std: float | None = None, layer: int = 0) -> dict:
+    """All nine parameter tensors in storage dtype (CPU).  Layer l > 0 of a
+    stack draws from seeds of its own (layer 0 is the single-layer draw)."""
     shapes = weight_shapes(w)
     gs = w.gamma_std if gamma_std is None else gamma_std
+
+    def sd(k):
+        return w.seed(k) if layer == 0 else [w.seed(k), layer]
+
     out = {}
     for k, name in enumerate(WEIGHT_NAMES, start=1):
-        out[name] = storage(normal_f32(w.seed(k), shapes[name], w.w_std), w.dtype)
+        out[name] = storage(normal_f32(sd(k), shapes[name], w.w_std), w.dtype)
     for k, name in enumerate(NORM_NAMES, start=8):
         if gs > 0:
-            g = normal_f32(w.seed(k), shapes[name], gs, mean=1.0)
+            g = normal_f32(sd(k), shapes[name], gs, mean=1.0)
         else:
             g = np.ones(shapes[name], np.float32)
         out[name] = storage(g, w.dtype)
     return out
+
+
+def final_norm_weight(w: Workload, gamma_std: float = 0.1) -> torch.Tensor:
+    """Gamma [d] of a stack's final RMSNorm: N(1, gamma_std^2) in storage dtype."""
+    return storage(normal_f32(w.seed(15), (w.hidden_size,), gamma_std, mean=1.0), w.dtype)
 
 
 def layer_input(w: Workload) -> torch.Tensor:

@@ -115,6 +115,7 @@ typedef struct {
 
 typedef struct llama_layer llama_layer;         /* opaque */
 typedef struct llama_kv_cache llama_kv_cache;   /* opaque */
+typedef struct llama_stack llama_stack;         /* opaque */
 
 const char* llama_status_string(llama_status s);
 
@@ -156,6 +157,23 @@ llama_status llama_kv_cache_create(const llama_layer_config* cfg, int32_t num_bl
                                    int32_t block_size, int32_t max_seqs,
                                    const int32_t* block_order, void* pool_dev,
                                    llama_kv_cache** out);
+
+/* The same for a stack of n_layers layers of config cfg: one K and one V pool
+ * per layer ("Chapter 10", section 8: the cache holds K and V for every
+ * layer), laid out [n_layers][num_blocks][...], all indexed by one set of
+ * block tables, so a sequence's block i holds the same 16 positions in every
+ * layer.  n_layers = 1 is the single-layer cache above.  On a cache with
+ * n_layers > 1, llama_kv_cache_write and llama_kv_cache_read move
+ * [n_layers, n, G, D] buffers (layer-major); llama_layer_prefill/decode
+ * reject it (LLAMA_ERR_SHAPE): it is used through llama_stack_*. */
+llama_status llama_kv_cache_bytes_layers(const llama_layer_config* cfg, int32_t n_layers,
+                                         int32_t num_blocks, int32_t block_size, int32_t max_seqs,
+                                         size_t* bytes);
+llama_status llama_kv_cache_create_layers(const llama_layer_config* cfg, int32_t n_layers,
+                                          int32_t num_blocks, int32_t block_size, int32_t max_seqs,
+                                          const int32_t* block_order, void* pool_dev,
+                                          llama_kv_cache** out);
+llama_status llama_kv_cache_num_layers(const llama_kv_cache* cache, int32_t* n_layers);
 llama_status llama_kv_cache_destroy(llama_kv_cache* cache);
 
 /* Open an empty sequence; its id is in [0, max_seqs). */
@@ -167,12 +185,14 @@ llama_status llama_kv_cache_seq_len(const llama_kv_cache* cache, int32_t seq_id,
 llama_status llama_kv_cache_free_blocks(const llama_kv_cache* cache, int32_t* n);
 
 /* Append n_tokens already-rotated keys and values ([n, G, D] each, device,
- * cfg.dtype) to a sequence (positions len .. len+n-1).  Used to restore a
- * saved cache or to pre-fill one. */
+ * cfg.dtype; [n_layers, n, G, D] for a multi-layer cache) to a sequence
+ * (positions len .. len+n-1).  Used to restore a saved cache or to pre-fill
+ * one. */
 llama_status llama_kv_cache_write(llama_kv_cache* cache, int32_t seq_id, int32_t n_tokens,
                                   const void* k_dev, const void* v_dev, void* stream);
 
-/* Copy positions start .. start+n-1 of a sequence into [n, G, D] buffers. */
+/* Copy positions start .. start+n-1 of a sequence into [n, G, D] buffers
+ * ([n_layers, n, G, D] for a multi-layer cache). */
 llama_status llama_kv_cache_read(const llama_kv_cache* cache, int32_t seq_id, int32_t start,
                                  int32_t n, void* k_dev, void* v_dev, void* stream);
 
@@ -194,6 +214,44 @@ llama_status llama_layer_prefill(llama_layer* layer, llama_kv_cache* cache, int3
  * x: [batch, d]; out: [batch, d] in out_dtype.
  * workspace: device, llama_layer_workspace_bytes(batch, batch). */
 llama_status llama_layer_decode(llama_layer* layer, llama_kv_cache* cache, int32_t batch,
+                                const int32_t* seq_ids, const void* x, void* out,
+                                int32_t out_dtype, void* workspace, void* stream);
+
+/* ---- stack of layers + final RMSNorm ---------------------------------- */
+
+/* The model-level use of the layer ("From Transformer to the LLaMA series",
+ * section 8, LlamaModel.forward; section 3.3 and self-test Q1: Pre-LN needs
+ * one more RMSNorm after the last block; "From Transformer to LLaMA: an
+ * overview", 4.1):
+ *   x_{l+1} = layer_l(x_l), l = 0 .. n_layers-1;  y = RMSNorm_final(x_L)
+ * The hidden state between layers (and into the final norm) is held in
+ * cfg.dtype.  The final norm uses the layers' rms_norm_eps.
+ *
+ * layers: n_layers handles created with identical configs (else
+ * LLAMA_ERR_SHAPE), run in array order; they must outlive the stack, and the
+ * stack does not own them.  final_norm: device [d] gamma in cfg.dtype,
+ * caller-owned, must outlive the stack. */
+llama_status llama_stack_create(llama_layer* const* layers, int32_t n_layers, const void* final_norm,
+                                llama_stack** out);
+
+/* Workspace bytes for stack calls with at most max_tokens tokens and
+ * max_batch sequences (one layer's workspace plus two [T, d] hidden-state
+ * buffers). */
+llama_status llama_stack_workspace_bytes(const llama_stack* stack, int32_t max_tokens, int32_t max_batch,
+                                         size_t* bytes);
+llama_status llama_stack_destroy(llama_stack* stack);
+
+/* Prefill / decode through every layer and the final norm, with the
+ * arguments and semantics of llama_layer_prefill / llama_layer_decode; cache
+ * must have been created with n_layers equal to the stack's (else
+ * LLAMA_ERR_SHAPE).  Layer l reads and appends the K/V of its own pools; the
+ * sequence lengths advance once per call.  out holds y.  Per-kernel timing
+ * is recorded by each layer's handle; the final norm ("rms_final_norm") is
+ * counted with the last layer. */
+llama_status llama_stack_prefill(llama_stack* stack, llama_kv_cache* cache, int32_t batch,
+                                 int32_t seq_len, const int32_t* seq_ids, const void* x,
+                                 void* out, int32_t out_dtype, void* workspace, void* stream);
+llama_status llama_stack_decode(llama_stack* stack, llama_kv_cache* cache, int32_t batch,
                                 const int32_t* seq_ids, const void* x, void* out,
                                 int32_t out_dtype, void* workspace, void* stream);
 

@@ -27,6 +27,10 @@ static int g_events = 0;
 static int g_uploads = 0;
 struct PackCall { int rows, cols, ldd, row_mul, row_add, head_pairs; bool gamma; };
 static std::vector<PackCall> g_packs;
+static std::vector<const void*> g_ins;   // x of each first-norm / final-norm launch
+static std::vector<void*> g_outs;        // out of each down-projection launch
+struct FinalCall { const void* gamma; void* y; };
+static FinalCall g_final = {nullptr, nullptr};
 
 namespace llk {
 int gemm_tile_n(GemmTile t) { return t == GemmTile::LARGE ? 256 : 64; }
@@ -38,13 +42,15 @@ size_t skinny_partial_bytes(int M, int N, int K) {
 hipError_t launch_gemm(DType, GemmTile t, const GemmArgs& a, hipStream_t) {
   const char* tag = t == GemmTile::LARGE ? "L" : (t == GemmTile::SKINNY ? "K" : "S");
   g_log.push_back("gemm" + std::to_string((int)a.epi) + tag);
+  if (a.epi == Epi::RESID_OUT) g_outs.push_back(a.out);
   if (t == GemmTile::SKINNY && a.split_ws_bytes < skinny_partial_bytes(a.M, a.N, a.K)) g_log.push_back("gemm-ws-short");
   return hipSuccess;
 }
 hipError_t launch_upload(const Upload& u, hipStream_t);
-hipError_t launch_rms_rowscale(DType t, const void*, float*, void* xt, int, int, float, const Upload* up,
+hipError_t launch_rms_rowscale(DType t, const void* x, float*, void* xt, int, int, float, const Upload* up,
                                hipStream_t s) {
   g_log.push_back("rms1");
+  g_ins.push_back(x);
   // bf16 layers get the tiled operand copy of x; fp32 layers read x directly
   if ((t == DType::BF16) != (xt != nullptr)) g_log.push_back("rms1-xt-mismatch");
   if (up) {  // the batch riding on this launch is applied like a standalone upload
@@ -55,6 +61,13 @@ hipError_t launch_rms_rowscale(DType t, const void*, float*, void* xt, int, int,
 }
 hipError_t launch_rms_convert(DType, const float*, const float*, void*, float*, int, int, float, hipStream_t) {
   g_log.push_back("rms2");
+  return hipSuccess;
+}
+hipError_t launch_rms_norm_out(DType, const void* x, const void* gamma, void* y, DType, int, int, float,
+                               hipStream_t) {
+  g_log.push_back("rms_final");
+  g_ins.push_back(x);
+  g_final = {gamma, y};
   return hipSuccess;
 }
 hipError_t launch_attn_prefill(DType, const void*, void*, int, const CacheView&, const BatchView&, hipStream_t) {
@@ -402,6 +415,145 @@ int main() {
     std::free(xb);
     std::free(ob);
     std::free(packed_b);
+  }
+  // ---- stack of 3 layers over one 3-layer cache ----
+  {
+    const int NL = 3;
+    std::vector<void*> packs;
+    std::vector<llama_layer*> Ls;
+    llama_layer_config cs = tiny();
+    for (int l = 0; l < NL; ++l) {
+      size_t pb = 0;
+      CHECK(llama_layer_packed_bytes(&cs, &pb) == LLAMA_OK);
+      packs.push_back(aligned_buf(pb));
+      llama_layer* Ll = nullptr;
+      CHECK(llama_layer_create(&cs, &w, packs.back(), nullptr, &Ll) == LLAMA_OK);
+      Ls.push_back(Ll);
+    }
+    void* gamma_f = aligned_buf(256 * 4);
+    llama_stack* S = nullptr;
+    CHECK(llama_stack_create(Ls.data(), 0, gamma_f, &S) == LLAMA_ERR_INVALID_ARG);
+    CHECK(llama_stack_create(Ls.data(), NL, nullptr, &S) == LLAMA_ERR_INVALID_ARG);
+    {
+      // a layer with another config does not join the stack
+      llama_layer_config co = cs;
+      co.rope_theta = 500000.f;
+      size_t pb = 0;
+      CHECK(llama_layer_packed_bytes(&co, &pb) == LLAMA_OK);
+      void* po = aligned_buf(pb);
+      llama_layer* Lo = nullptr;
+      CHECK(llama_layer_create(&co, &w, po, nullptr, &Lo) == LLAMA_OK);
+      llama_layer* mixed[2] = {Ls[0], Lo};
+      CHECK(llama_stack_create(mixed, 2, gamma_f, &S) == LLAMA_ERR_SHAPE && S == nullptr);
+      CHECK(llama_layer_destroy(Lo) == LLAMA_OK);
+      std::free(po);
+    }
+    CHECK(llama_stack_create(Ls.data(), NL, gamma_f, &S) == LLAMA_OK && S != nullptr);
+    size_t b1 = 0, b3 = 0;
+    CHECK(llama_kv_cache_bytes_layers(&cs, 1, 6, 16, 2, &b1) == LLAMA_OK);
+    CHECK(llama_kv_cache_bytes(&cs, 6, 16, 2, &bytes) == LLAMA_OK && bytes == b1);
+    CHECK(llama_kv_cache_bytes_layers(&cs, NL, 6, 16, 2, &b3) == LLAMA_OK);
+    const size_t layer_pool = (size_t)6 * 2 * 16 * 64 * 4;  // blocks x G x 16 x D x 4 bytes
+    CHECK(b3 == b1 + 2 * (NL - 1) * layer_pool);
+    CHECK(llama_kv_cache_bytes_layers(&cs, 0, 6, 16, 2, &b3) == LLAMA_ERR_INVALID_ARG);
+    void* pool3 = aligned_buf(b3);
+    llama_kv_cache* C3 = nullptr;
+    CHECK(llama_kv_cache_create_layers(&cs, NL, 6, 16, 2, nullptr, pool3, &C3) == LLAMA_OK);
+    int32_t nl = 0;
+    CHECK(llama_kv_cache_num_layers(C3, &nl) == LLAMA_OK && nl == NL);
+    int32_t sa = -1, sb = -1;
+    CHECK(llama_kv_cache_add_seq(C3, &sa) == LLAMA_OK && llama_kv_cache_add_seq(C3, &sb) == LLAMA_OK);
+    int32_t sids[2] = {sa, sb};
+    size_t wsz = 0, lwsz = 0;
+    CHECK(llama_stack_workspace_bytes(S, 40, 2, &wsz) == LLAMA_OK);
+    CHECK(llama_layer_workspace_bytes(Ls[0], 40, 2, &lwsz) == LLAMA_OK);
+    CHECK(wsz >= lwsz + 2 * 40 * 256 * 4);
+    void* ws3 = aligned_buf(wsz);
+    void* x3 = aligned_buf(40 * 256 * 4);
+    void* y3 = aligned_buf(40 * 256 * 4);
+    // a multi-layer cache is the stack's; a single-layer cache is the layer's
+    CHECK(llama_layer_prefill(Ls[0], C3, 2, 20, sids, x3, y3, LLAMA_DTYPE_F32, ws3, nullptr) == LLAMA_ERR_SHAPE);
+    llama_kv_cache* C1 = nullptr;
+    void* pool1 = aligned_buf(b1);
+    CHECK(llama_kv_cache_create(&cs, 6, 16, 2, nullptr, pool1, &C1) == LLAMA_OK);
+    int32_t s1a = -1;
+    CHECK(llama_kv_cache_add_seq(C1, &s1a) == LLAMA_OK);
+    CHECK(llama_stack_prefill(S, C1, 1, 20, &s1a, x3, y3, LLAMA_DTYPE_F32, ws3, nullptr) == LLAMA_ERR_SHAPE);
+    CHECK(llama_kv_cache_destroy(C1) == LLAMA_OK);
+    std::free(pool1);
+    CHECK(llama_stack_prefill(S, C3, 2, 20, sids, x3, y3, LLAMA_DTYPE_BF16, ws3, nullptr) == LLAMA_ERR_DTYPE);
+
+    g_log.clear();
+    g_ins.clear();
+    g_outs.clear();
+    CHECK(llama_stack_prefill(S, C3, 2, 20, sids, x3, y3, LLAMA_DTYPE_F32, ws3, nullptr) == LLAMA_OK);
+    {
+      std::vector<std::string> want;
+      for (int l = 0; l < NL; ++l)
+        for (const char* k : {"rms1", "gemm0S", "attn_prefill", "gemm1S", "rms2", "gemm2S", "gemm3S"}) want.push_back(k);
+      want.push_back("rms_final");
+      CHECK(g_log == want);
+    }
+    // layer l + 1 reads what layer l wrote, the final norm reads the last layer's output
+    CHECK(g_ins.size() == NL + 1 && g_outs.size() == NL);
+    if (g_ins.size() == NL + 1 && g_outs.size() == NL) {
+      CHECK(g_ins[0] == x3);
+      for (int l = 0; l < NL; ++l) CHECK(g_ins[l + 1] == g_outs[l] && g_outs[l] != y3);
+      CHECK(g_outs[0] != g_outs[1] && g_outs[1] != g_outs[2] && g_outs[0] == g_outs[2]);
+    }
+    CHECK(g_final.gamma == gamma_f && g_final.y == y3);
+    CHECK(llama_kv_cache_seq_len(C3, sa, &n) == LLAMA_OK && n == 20);  // advanced once
+    CHECK(llama_kv_cache_free_blocks(C3, &n) == LLAMA_OK && n == 2);
+    g_log.clear();
+    CHECK(llama_stack_decode(S, C3, 2, sids, x3, y3, LLAMA_DTYPE_F32, ws3, nullptr) == LLAMA_OK);
+    CHECK(g_log.size() == NL * 8 + 1 && g_log.back() == "rms_final" && g_log[2] == "attn_decode");
+    CHECK(llama_kv_cache_seq_len(C3, sb, &n) == LLAMA_OK && n == 21);
+    // per-layer pools: K/V written as [NL, n, G, D] come back per layer, unaliased
+    {
+      int32_t sc = -1;
+      CHECK(llama_kv_cache_free_seq(C3, sb) == LLAMA_OK && llama_kv_cache_add_seq(C3, &sc) == LLAMA_OK);
+      const int ntok = 19, G = 2, D = 64;
+      const size_t per = (size_t)ntok * G * D;
+      std::vector<float> k(NL * per), v(NL * per), k2(NL * per), v2(NL * per);
+      for (size_t i = 0; i < k.size(); ++i) {
+        k[i] = (float)i;
+        v[i] = 0.5f - (float)i;
+      }
+      CHECK(llama_kv_cache_write(C3, sc, ntok, k.data(), v.data(), nullptr) == LLAMA_OK);
+      CHECK(llama_kv_cache_read(C3, sc, 0, ntok, k2.data(), v2.data(), nullptr) == LLAMA_OK);
+      CHECK(k == k2 && v == v2);
+      // layer 1's K pool starts one layer's pool after layer 0's
+      const float* kp = (const float*)pool3;
+      int32_t blk0 = -1;
+      {
+        // first block of sc is the block at the table slot of sc
+        const size_t tabo = 2 * ((NL * layer_pool + 255) & ~size_t(255));
+        blk0 = ((const int32_t*)((char*)pool3 + tabo))[sc * 5 + 0];
+      }
+      const size_t lp = layer_pool / 4;
+      CHECK(kp[lp + ((size_t)blk0 * G * 16) * D] == (float)per);  // layer 1, position 0, head 0, d 0
+      CHECK(kp[2 * lp + ((size_t)blk0 * G * 16) * D + 5] == (float)(2 * per + 5));
+    }
+    {
+      CHECK(llama_layer_profile_enable(Ls[NL - 1], 1) == LLAMA_OK);
+      CHECK(llama_stack_decode(S, C3, 1, sids, x3, y3, LLAMA_DTYPE_F32, ws3, nullptr) == LLAMA_OK);
+      llama_kernel_time kt[16];
+      int32_t nk = 0;
+      CHECK(llama_layer_profile_read(Ls[NL - 1], kt, 16, &nk, 1) == LLAMA_OK && nk == 9);
+      bool seen = false;
+      for (int i = 0; i < nk; ++i) seen |= std::string(kt[i].name) == "rms_final_norm";
+      CHECK(seen);
+      CHECK(llama_layer_profile_enable(Ls[NL - 1], 0) == LLAMA_OK);
+    }
+    CHECK(llama_stack_destroy(S) == LLAMA_OK);
+    CHECK(llama_kv_cache_destroy(C3) == LLAMA_OK);
+    for (llama_layer* Ll : Ls) CHECK(llama_layer_destroy(Ll) == LLAMA_OK);
+    for (void* p : packs) std::free(p);
+    std::free(gamma_f);
+    std::free(pool3);
+    std::free(ws3);
+    std::free(x3);
+    std::free(y3);
   }
   std::free(pool);
   std::free(ws);

@@ -21,6 +21,24 @@ TOL = {"f32": {"max_rel": 1e-4}, "bf16": {"max_rel": 3e-2, "mean_rel": 3e-3},
        "bf16_gamma": {"max_rel": 3e-2, "mean_rel": 4e-3}}
 
 
+def stack_tol(dtype: str, n_layers: int) -> str:
+    """Tolerance key of an n-layer stack compared at its output.
+
+    Each layer adds an error within the single-layer limits (its own bf16
+    roundings), and the error already in its input reaches its output through
+    the residual path with gain about one; the final RMSNorm rescales the
+    output to unit RMS, which keeps the errors relative.  Summing the n
+    contributions (triangle inequality) scales the single-layer limits by n.
+    (Independent contributions would add in quadrature, sqrt(n); a 3-layer
+    LLaMA-3-8B-shaped stack at 300 tokens measures about 2.1 times the
+    single-layer mean error, between the two.)
+    """
+    key = f"{dtype}_stack{n_layers}"
+    if key not in TOL:
+        TOL[key] = {k: v * n_layers for k, v in TOL[dtype].items()}
+    return key
+
+
 def errors(gpu, ref) -> dict:
     g = np.asarray(gpu, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)

@@ -1,0 +1,105 @@
+"""GPU parity of the layer stack (N layers over one multi-layer paged cache,
+then the final RMSNorm) against the float64 stack oracle.
+
+The oracle rounds the hidden state to the storage dtype between layers, as
+the stack holds it; the tolerances of a stack are those of one layer, scaled
+as derived in tests/parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decoder_block_amd import synth
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _stack(w, n_layers, gamma_std=None):
+    from decoder_block_amd.llama_layer import DecoderStack
+    ws = [synth.layer_weights(w, gamma_std, layer=l) for l in range(n_layers)]
+    wo = [{k: synth.as_f64(v) for k, v in d.items()} for d in ws]
+    layers = [P.make_layer(w, d, max_position=w.positions_needed() + 8) for d in ws]
+    gf = synth.final_norm_weight(w)
+    return DecoderStack(layers, gf), wo, synth.as_f64(gf)
+
+
+def test_tiny_fp32_stack_prefill_decode_and_caches():
+    w = W[1]
+    NL = 3
+    stack, wo, gf = _stack(w, NL)
+    nb = (w.seq_len + 4 + 15) // 16
+    cache = stack.cache(nb, 1, block_order=np.random.Generator(np.random.PCG64(2)).permutation(nb).tolist())
+    sid = cache.add_seq()
+    x = synth.layer_input(w)
+    y = stack.prefill(cache, [sid], x.cuda())
+    torch.cuda.synchronize()
+    ref, k_ref, v_ref = oracle.stack_prefill(w.config_dict(), wo, gf, synth.as_f64(x), "f32")
+    e = P.assert_close(P.to_np(y), ref, "f32", "stack prefill")
+    print("fp32 stack prefill", e)
+    k, v = cache.read(sid, 0, w.seq_len)
+    for l in range(NL):
+        P.assert_close(P.to_np(k[l]), k_ref[l, 0], "f32", f"layer {l} cached K")
+        P.assert_close(P.to_np(v[l]), v_ref[l, 0], "f32", f"layer {l} cached V")
+    caches = [[(k_ref[l, 0], v_ref[l, 0])] for l in range(NL)]
+    for step in range(4):
+        xt = synth.decode_input(w, step)
+        o = stack.decode(cache, [sid], xt.cuda())
+        torch.cuda.synchronize()
+        r, caches = oracle.stack_decode_step(w.config_dict(), wo, gf, synth.as_f64(xt), caches, "f32")
+        P.assert_close(P.to_np(o), r, "f32", f"stack decode step {step}")
+    assert cache.seq_len(sid) == w.seq_len + 4
+
+
+def test_bf16_stack_prefill_and_decode():
+    w = synth.scaled(W[3], batch=2, seq_len=300)
+    NL = 3
+    stack, wo, gf = _stack(w, NL)
+    nb = w.batch * ((w.seq_len + 2 + 15) // 16)
+    order = np.random.Generator(np.random.PCG64(21)).permutation(nb).tolist()
+    cache = stack.cache(nb, w.batch, block_order=order)
+    sids = [cache.add_seq() for _ in range(w.batch)]
+    x = synth.layer_input(w)
+    y = stack.prefill(cache, sids, x.cuda())
+    torch.cuda.synchronize()
+    ref, k_ref, v_ref = oracle.stack_prefill(w.config_dict(), wo, gf, synth.as_f64(x), "bf16")
+    e = P.assert_close(P.to_np(y), ref, P.stack_tol("bf16", NL), "bf16 stack prefill")
+    print("bf16 stack prefill", e)
+    k, v = cache.read(sids[1], 0, w.seq_len)
+    P.assert_close(P.to_np(k[NL - 1]), k_ref[NL - 1, 1], P.stack_tol("bf16", NL - 1), "last layer cached K")
+    P.assert_close(P.to_np(v[NL - 1]), v_ref[NL - 1, 1], P.stack_tol("bf16", NL - 1), "last layer cached V")
+    caches = [[(k_ref[l, b], v_ref[l, b]) for b in range(w.batch)] for l in range(NL)]
+    for step in range(2):
+        xt = synth.decode_input(w, step)
+        o = stack.decode(cache, sids, xt.cuda(), out_dtype="bf16")
+        torch.cuda.synchronize()
+        r, caches = oracle.stack_decode_step(w.config_dict(), wo, gf, synth.as_f64(xt), caches, "bf16")
+        e = P.assert_close(P.to_np(o), r, P.stack_tol("bf16", NL), f"bf16 stack decode step {step}")
+        print("bf16 stack decode", step, e)
+
+
+def test_one_layer_stack_is_the_layer_then_the_final_norm():
+    # same kernels on the same input: the cached K/V agree bit for bit, and
+    # the stack's output is the final RMSNorm of the layer's bf16 output
+    w = synth.scaled(W[3], batch=1, seq_len=200)
+    from decoder_block_amd.llama_layer import DecoderStack
+    ws, _ = P.weights_for(w)
+    layer = P.make_layer(w, ws)
+    gf = synth.final_norm_weight(w)
+    stack = DecoderStack([layer], gf)
+    x = synth.layer_input(w).cuda()
+    nb = (w.seq_len + 15) // 16
+    c1 = P.make_cache(layer, w, w.seq_len, 1)
+    out1, s1 = P.gpu_prefill(layer, c1, x, out_dtype="bf16")
+    c2 = stack.cache(nb, 1)
+    s2 = c2.add_seq()
+    y = stack.prefill(c2, [s2], x, out_dtype="f32")
+    torch.cuda.synchronize()
+    k1, v1 = c1.read(s1[0], 0, w.seq_len)
+    k2, v2 = c2.read(s2, 0, w.seq_len)
+    assert torch.equal(k1, k2) and torch.equal(v1, v2)
+    ref = oracle.rms_norm(P.to_np(out1), synth.as_f64(gf), w.rms_norm_eps)
+    P.assert_close(P.to_np(y), ref, "f32", "final norm of the layer output")
