@@ -8,11 +8,13 @@ pre-filled at context lengths drawn from U[512, 8192]), reported under
 "decode".  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--decode-steps N] [--no-cpu-baseline]
-                    [--prefill-workload NAME] [--decode-workload NAME]
+                    [--prefill-workload NAME] [--decode-workload NAME] [--stack-layers N]
 
 The workload options time the other shapes with the same step definition:
 the LLaMA-2-7B (MHA) and LLaMA-3-70B layers, and the GQA ratio sweep (MQA at
-the 8B shape, the LLaMA-3-405B layer); the defaults are the 8B jobs above.
+the 8B shape, the LLaMA-3-405B layer); the defaults are the 8B jobs above.  --stack-layers N times N such layers
+(each with its own weights, over one N-layer paged cache) plus the final
+RMSNorm as the step instead of one layer.
 """
 from __future__ import annotations
 
@@ -76,45 +78,79 @@ def prefill_flops(w) -> dict:
             "gemm_down_resid": 2 * T * I * d}
 
 
+def make_model(args, L, synth, w, max_pos):
+    """The layer, or (--stack-layers N > 1) a stack of N layers with their own
+    weights and the final RMSNorm; returns (runner, [layer handles])."""
+    nl = args.stack_layers
+    layers = []
+    for l in range(nl):
+        ws = synth.layer_weights(w, layer=l)
+        layers.append(L.DecoderLayer(w.config_dict(), ws, "bf16", max_pos))
+        del ws
+    if nl == 1:
+        return layers[0], layers
+    return L.DecoderStack(layers, synth.final_norm_weight(w)), layers
+
+
+def make_cache(L, model, layers, nb, batch, order=None):
+    if len(layers) == 1:
+        return L.PagedKVCache(model, nb, batch, block_order=order)
+    return model.cache(nb, batch, block_order=order)
+
+
+def profile_all(L, layers, on):
+    for layer in layers:
+        L.llama_layer_profile_enable(layer.handle, on)
+
+
+def profile_sum(L, layers):
+    """Per-kernel (launches, total ms) summed over the layers."""
+    tot = {}
+    for layer in layers:
+        for name, (n, ms) in L.llama_layer_profile_read(layer.handle, reset=True).items():
+            a, b = tot.get(name, (0, 0.0))
+            tot[name] = (a + n, b + ms)
+    return tot
+
+
 def run_prefill(args, torch, L, synth):
     w = synth.PREFILL_JOBS[args.prefill_workload]
-    log(f"[bench] prefill workload {w.name}: generating weights")
-    ws = synth.layer_weights(w)
-    layer = L.DecoderLayer(w.config_dict(), ws, "bf16", w.positions_needed())
-    del ws
+    nl = args.stack_layers
+    log(f"[bench] prefill workload {w.name}" + (f", stack of {nl} layers" if nl > 1 else "") + ": generating weights")
+    model, layers = make_model(args, L, synth, w, w.positions_needed())
     x = synth.layer_input(w).cuda()
-    cache = L.PagedKVCache(layer, w.batch * ((w.seq_len + 15) // 16), w.batch)
+    cache = make_cache(L, model, layers, w.batch * ((w.seq_len + 15) // 16), w.batch)
     out = torch.empty((w.batch, w.seq_len, w.hidden_size), dtype=torch.bfloat16, device="cuda")
 
     def step():
         sids = [cache.add_seq() for _ in range(w.batch)]
-        layer.prefill(cache, sids, x, out_dtype="bf16", out=out)
+        model.prefill(cache, sids, x, out_dtype="bf16", out=out)
         for s in sids:
             cache.free_seq(s)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    L.llama_layer_profile_enable(layer.handle, True)
+    profile_all(L, layers, True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    prof = L.llama_layer_profile_read(layer.handle, reset=True)
-    L.llama_layer_profile_enable(layer.handle, False)
+    prof = profile_sum(L, layers)
+    profile_all(L, layers, False)
     ms = (t1 - t0) * 1e3 / args.steps
-    flops = prefill_flops(w)
+    flops = {k: v * nl for k, v in prefill_flops(w).items()}
     kern = {}
     for name, (n, tot) in prof.items():
         avg = tot / n
         kern[name] = {"avg_ms": round(avg, 4), "launches": n}
         if name in flops:
-            kern[name]["tflops"] = round(flops[name] / (avg * 1e-3) / 1e12, 1)
+            kern[name]["tflops"] = round(flops[name] / nl / (avg * 1e-3) / 1e12, 1)  # per launch
     dom = "gemm_gate_up_swiglu"
     dom_ms = prof[dom][1] / prof[dom][0]
-    ach = flops[dom] / (dom_ms * 1e-3) / 1e12
+    ach = flops[dom] / nl / (dom_ms * 1e-3) / 1e12
     total_flops = sum(flops.values())
     rec = traffic_record(dom)
     traffic = int(rec["bytes_per_launch"]) if rec and "bytes_per_launch" in rec else None
@@ -124,38 +160,41 @@ def run_prefill(args, torch, L, synth):
         "layer_tflops": total_flops / (ms * 1e-3) / 1e12,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "flops_per_launch": flops[dom], "avg_launch_ms": round(dom_ms, 4)},
+                     "flops_per_launch": flops[dom] // nl, "avg_launch_ms": round(dom_ms, 4)},
     }
-    layer.close()
     cache.close()
+    model.close()
+    for layer in layers:
+        layer.close()
     return w, res
 
 
 def run_decode(args, torch, L, synth):
     w = synth.DECODE_JOBS[args.decode_workload]
     log(f"[bench] decode workload {w.name}: weights and cache")
-    ws = synth.layer_weights(w)
     # positions for the warm-up, timed and profiled steps past the longest context
     max_pos = w.ctx_hi + 2 * args.decode_steps + args.decode_warmup + 1
-    layer = L.DecoderLayer(w.config_dict(), ws, "bf16", max_pos)
-    del ws
+    model, layers = make_model(args, L, synth, w, max_pos)
+    nl = len(layers)
     lens = synth.context_lengths(w)
     nsteps = args.decode_steps
     # room for warm-up, the timed steps and the profiled repeat of them
     nb = int(sum((int(l) + 2 * nsteps + args.decode_warmup + 15) // 16 for l in lens))
     perm = synth.block_permutation(w, nb).tolist()
-    cache = L.PagedKVCache(layer, nb, w.batch, block_order=perm)
+    cache = make_cache(L, model, layers, nb, w.batch, order=perm)
     sids = []
     for b in range(w.batch):
         sid = cache.add_seq()
         k, v = synth.cache_contents(w, b, int(lens[b]))
+        if nl > 1:  # the same contents in every layer's pool
+            k, v = k.expand(nl, *k.shape), v.expand(nl, *v.shape)
         cache.write(sid, k.cuda(), v.cuda())
         sids.append(sid)
     xs = [synth.decode_input(w, s).cuda() for s in range(nsteps + args.decode_warmup)]
     out = torch.empty((w.batch, w.hidden_size), dtype=torch.bfloat16, device="cuda")
     torch.cuda.synchronize()
     for s in range(args.decode_warmup):
-        layer.decode(cache, sids, xs[s], out_dtype="bf16", out=out)
+        model.decode(cache, sids, xs[s], out_dtype="bf16", out=out)
     torch.cuda.synchronize()
     ctx_start = np.array([cache.seq_len(s) for s in sids], dtype=np.int64)
     # timed steps without per-kernel events (at microsecond kernels the event
@@ -163,29 +202,29 @@ def run_decode(args, torch, L, synth):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(nsteps):
-        layer.decode(cache, sids, xs[args.decode_warmup + s], out_dtype="bf16", out=out)
+        model.decode(cache, sids, xs[args.decode_warmup + s], out_dtype="bf16", out=out)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     us = (t1 - t0) * 1e6 / nsteps
     # ... then the same number of steps again with per-kernel HIP events on the
     # layer's stream, for the kernel breakdown (context now longer by nsteps)
     ctx_prof = np.array([cache.seq_len(s) for s in sids], dtype=np.int64)
-    L.llama_layer_profile_enable(layer.handle, True)
+    profile_all(L, layers, True)
     for s in range(nsteps):
-        layer.decode(cache, sids, xs[args.decode_warmup + s], out_dtype="bf16", out=out)
+        model.decode(cache, sids, xs[args.decode_warmup + s], out_dtype="bf16", out=out)
     torch.cuda.synchronize()
     t2 = time.perf_counter()
-    prof = L.llama_layer_profile_read(layer.handle, reset=True)
-    L.llama_layer_profile_enable(layer.handle, False)
+    prof = profile_sum(L, layers)
+    profile_all(L, layers, False)
     us_prof = (t2 - t1) * 1e6 / nsteps
     G, D = w.num_key_value_heads, w.head_dim
     # keys read per step: every cached key plus the new one, K and V, once per KV group
     keys = float(np.sum(ctx_start + 1)) + w.batch * (nsteps - 1) / 2.0
-    kv_bytes = keys * G * D * 2 * 2
+    kv_bytes = keys * G * D * 2 * 2 * nl
     keys_prof = float(np.sum(ctx_prof + 1)) + w.batch * (nsteps - 1) / 2.0
-    kv_bytes_prof = keys_prof * G * D * 2 * 2
+    kv_bytes_prof = keys_prof * G * D * 2 * 2  # one layer's (one launch of the attention kernel)
     d, I, H = w.hidden_size, w.intermediate_size, w.num_attention_heads
-    weight_bytes = 2 * (d * (H + 2 * G) * D + H * D * d + 3 * d * I)
+    weight_bytes = 2 * (d * (H + 2 * G) * D + H * D * d + 3 * d * I) * nl
     dom = "attn_decode_split"
     dom_ms = prof[dom][1] / prof[dom][0]
     ach = kv_bytes_prof / (dom_ms * 1e-3) / 1e9
@@ -205,8 +244,10 @@ def run_decode(args, torch, L, synth):
                      "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": kv_bytes_prof, "avg_launch_ms": round(dom_ms, 4)},
     }
-    layer.close()
     cache.close()
+    model.close()
+    for layer in layers:
+        layer.close()
     return res
 
 
@@ -253,7 +294,11 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows (>= S: the whole layer)")
     ap.add_argument("--prefill-workload", default="llama3-8b-layer-prefill", choices=sorted(synth.PREFILL_JOBS))
     ap.add_argument("--decode-workload", default="llama3-8b-layer-decode", choices=sorted(synth.DECODE_JOBS))
+    ap.add_argument("--stack-layers", type=int, default=1,
+                    help="N > 1: time a stack of N layers (own weights) plus the final RMSNorm")
     args = ap.parse_args()
+    if args.stack_layers < 1:
+        ap.error("--stack-layers must be at least 1")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -277,7 +322,8 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seq_len": w.seq_len, "hidden_size": w.hidden_size,
                    "intermediate_size": w.intermediate_size, "num_attention_heads": w.num_attention_heads,
                    "num_key_value_heads": w.num_key_value_heads, "rope_theta": w.rope_theta,
-                   "rms_norm_eps": w.rms_norm_eps},
+                   "rms_norm_eps": w.rms_norm_eps,
+                   **({"stack_layers": args.stack_layers} if args.stack_layers > 1 else {})},
         "layer_tflops": round(pre["layer_tflops"], 1),
         "layer_mfma_frac": round(pre["layer_tflops"] / PEAK_BF16_TFLOPS, 4),
         "roofline": pre["roofline"],
