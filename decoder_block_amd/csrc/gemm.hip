@@ -735,10 +735,12 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // Skinny bf16 GEMM for few tokens (decode): the weights are streamed once from
 // HBM and the work is bound by that stream, so the shape is chosen for memory
-// parallelism, not reuse.  One workgroup per CU, each owning 64 features x 64
-// tokens and one of KS slices of K.  K is split into the largest power of two
-// of slices that keeps the workgroups within one round of the 256 CUs (each
-// further round pays the pipeline ramp-up again), with at least two 64-deep
+// parallelism, not reuse.  Workgroups of 64 features x 64 tokens and one of
+// KS slices of K, two resident per CU (a 64 KB ring each), so that a launch
+// of more workgroups than CUs (448 for the 8B gate/up) has them all in flight
+// at once.  K is split into the largest power of two of slices that keeps the
+// workgroups within 256 (more, shorter slices measured slower: each pays the
+// pipeline ramp-up, and the partial sums grow), with at least two 64-deep
 // stages per slice.  With KS = 1 the epilogue runs directly, otherwise the
 // fp32 partial goes to [ks][M][N] and a second pass adds the KS partials in a
 // fixed order and runs the epilogue.
@@ -766,12 +768,13 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int 
 // Weight-streaming bf16 GEMM for few tokens, staged through LDS.  A workgroup
 // owns 64 features x 64 tokens and one of KS slices of K.  Stages of 64
 // K-elements (W: 64 rows x 128 B, X: 64 rows x 128 B) are moved by LDS DMA
-// into a ring of NSL slots, NSL - 1 stages ahead, each DMA instruction
+// into a ring of NSL slots, NSL - 1 stages ahead (8 slots and one workgroup
+// per CU measured 3-8% slower on the 8B shapes), each DMA instruction
 // fetching whole 128-byte row segments.  Wave w computes features 16w..16w+15
 // for all 64 tokens, so no cross-wave reduction is needed.
 // ---------------------------------------------------------------------------
 struct StreamCfg {
-  static constexpr int NSL = 8;                 // ring slots
+  static constexpr int NSL = 4;                 // ring slots (64 KB: two workgroups per CU)
   static constexpr int CPR = 8;                 // 16-byte chunks per row per stage (64 bf16)
   static constexpr int ROWS = 128;              // 64 W rows, then 64 X rows
   static constexpr int SLOT = ROWS * CPR;       // chunks per slot (16 KB)
@@ -782,7 +785,7 @@ struct StreamCfg {
 };
 
 template <int EPI>
-__global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a, int KS) {
+__global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmArgs a, int KS) {
   using C = StreamCfg;
   __shared__ u32x4 ring[C::NSL * C::SLOT];
   const int n0 = blockIdx.x * 64, m0 = blockIdx.y * 64, ks = blockIdx.z;
