@@ -373,3 +373,34 @@ def test_llama3_405b_layer_prefill_sampled_rows_and_decode():
     r, _ = oracle.decode_step(_cfg(w), wo, synth.as_f64(xt), [(k_ref[b], v_ref[b]) for b in range(w.batch)])
     e = P.assert_close(P.to_np(o), r, "bf16", "405B decode")
     print("405B decode", e)
+
+
+@pytest.mark.parametrize("name,n_random,edge", [("llama3-8b-mqa-layer-prefill", 448, 64),
+                                                ("llama3-405b-layer-prefill", 32, 8)])
+def test_gqa_sweep_full_size_prefill_sampled_rows(name, n_random, edge):
+    # the sweep variants at the sizes bench.py times (B 1, S 8192), compared on
+    # a seeded row sample; the 405B weights are built outside the shared cache
+    w = synth.VARIANTS[name]
+    ws = synth.layer_weights(w)
+    wo = {k: synth.as_f64(v) for k, v in ws.items()}
+    layer = P.make_layer(w, ws)
+    del ws
+    x = synth.layer_input(w)
+    cache = P.make_cache(layer, w, w.seq_len, w.batch)
+    out, _ = P.gpu_prefill(layer, cache, x, out_dtype="bf16")
+    rows = synth.sample_rows(w, w.seq_len, n_random=n_random, edge=edge)
+    ref, _, _ = oracle.prefill(_cfg(w), wo, synth.as_f64(x), rows=rows)
+    e = P.assert_close(P.to_np(out)[:, rows], ref, "bf16", w.name)
+    print(w.name, len(rows), "rows", e)
+
+
+def test_mqa_decode_batch64_full_contexts():
+    w = synth.VARIANTS["llama3-8b-mqa-layer-decode"]
+    layer, cache, sids, host, wo = _decode_setup(w)
+    xt = synth.decode_input(w, 0)
+    o = layer.decode(cache, sids, xt.cuda())
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_step(_cfg(w), wo, synth.as_f64(xt), host)
+    e = P.assert_close(P.to_np(o), ref, "bf16", "MQA decode B=64")
+    print("MQA decode B=64", e)
+
