@@ -134,7 +134,6 @@ __global__ __launch_bounds__(512) void attn_prefill_f32_kernel(const T* __restri
   wmin = __builtin_amdgcn_readfirstlane(wmin);
   const int last_s = min(S, (rb + 1) * P) - 1;
   const int ntiles = (start + last_s) / C::KT + 1;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
 
   // Q fragments (B operand of S^T), resident for the whole key loop
   vec qf[C::RB][C::NQ];
