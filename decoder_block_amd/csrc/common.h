@@ -96,10 +96,6 @@ DEVI int lane_id() { return __lane_id(); }
 // templates using them still get their host-side launch stubs.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
-// LDS DMA: each lane's 16 bytes at g land at lds_base + 16 * lane (lds_base wave-uniform).
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(g, lds_base, 16, 0, 0);
-}
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
 // Workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations, not for its outstanding global loads / LDS DMAs (which
@@ -133,24 +129,20 @@ DEVI i32x4 make_rsrc(const void* base, uint32_t bytes) {
   const uint64_t a = reinterpret_cast<uint64_t>(base);
   return i32x4{(int32_t)(uint32_t)a, (int32_t)(uint32_t)(a >> 32), (int32_t)bytes, 0x00020000};
 }
-__device__ void llvm_amdgcn_raw_buffer_load_lds(i32x4 rsrc, __attribute__((address_space(3))) uint32_t* lds,
-                                                int size, int voffset, int soffset, int offset,
-                                                int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
-// Buffer LDS DMA: lane i's 16 bytes at (rsrc base + voffset) land at lds_base + 16 i.
-__device__ __forceinline__ void buf_dma16(i32x4 rsrc, void* lds_base, int voffset) {
-  llvm_amdgcn_raw_buffer_load_lds(rsrc, (__attribute__((address_space(3))) uint32_t*)(lds_base), 16, voffset, 0,
-                                  0, 0);
-}
 // LDS byte address of a __shared__ object (wave-uniform).
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
 }
-// The same DMA written as inline assembly, to the LDS byte address lds (an
-// SGPR value).  The compiler then does not know that it writes LDS, so it
-// never makes an LDS read wait for it (it cannot always tell slots of a ring
-// apart and would otherwise drain every outstanding DMA before each read):
-// the caller orders LDS itself, with wait_vmcnt and a barrier between a
-// stage's DMAs and the reads of that stage.
+// Buffer LDS DMA (lane i's 16 bytes at rsrc base + voffset land at lds + 16 i)
+// written as inline assembly, to the LDS byte address lds (an SGPR value).
+// The compiler then does not know that it writes LDS, so it never makes an
+// LDS read wait for it (it cannot always tell slots of a ring apart and would
+// otherwise drain every outstanding DMA before each read): the caller orders
+// LDS itself, with wait_vmcnt and a barrier between a stage's DMAs and the
+// reads of that stage.  The asm sets M0 (the DMA's LDS base).  The compiler
+// warns that M0 is a reserved register; nothing else in these kernels uses M0
+// (no compiler-generated LDS DMA, GWS, message or indexed-register
+// instructions), so no compiler-held M0 value can be disturbed.
 __device__ __forceinline__ void buf_dma16_to(i32x4 rsrc, uint32_t lds, int voffset) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(lds), "v"(voffset), "s"(rsrc)
                : "memory", "m0");
