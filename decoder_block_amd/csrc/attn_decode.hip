@@ -53,6 +53,52 @@ DEVI u32x4 keep_first(u32x4 w, int n) {
   return w;
 }
 
+// Work unit u of a launch -> (sequence b, 1024-key chunk c); b = -1 past the
+// last unit.  The units are every full chunk first, sequence by sequence, then
+// the partial last chunk of each sequence that has one, so the launch has no
+// empty workgroups and its last workgroups are the shorter partial chunks.
+// Each wave derives the map from the batch's lengths (scans over 64
+// sequences at a time); every lane gets the same (b, c).
+DEVI void unit_chunk(const BatchView& batch, int u, int lane, int& b, int& c) {
+  const int B = batch.batch;
+  int base = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {  // full chunks
+    const int bb = b0 + lane;
+    const int f = bb < B ? (batch.desc[2 * bb + 1] + 1) / kChunkKeys : 0;
+    int incl = f;  // inclusive prefix sum over the lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    const int tot = __shfl(incl, 63, 64);
+    if (u < base + tot) {
+      const int ln = __ffsll((unsigned long long)__ballot(incl > u - base)) - 1;
+      b = b0 + ln;
+      c = u - base - (__shfl(incl, ln, 64) - __shfl(f, ln, 64));
+      return;
+    }
+    base += tot;
+  }
+  for (int b0 = 0; b0 < B; b0 += 64) {  // partial chunks
+    const int bb = b0 + lane;
+    const int len = bb < B ? batch.desc[2 * bb + 1] + 1 : 0;
+    const bool part = bb < B && len % kChunkKeys != 0;
+    const unsigned long long m = __ballot(part);
+    const int cnt = __popcll(m);
+    if (u < base + cnt) {  // the (u - base)-th sequence of this group with a partial chunk
+      const bool mine = part && __popcll(m & ((1ull << lane) - 1)) == u - base;
+      const int ln = __ffsll((unsigned long long)__ballot(mine)) - 1;
+      b = b0 + ln;
+      c = __shfl(len, ln, 64) / kChunkKeys;
+      return;
+    }
+    base += cnt;
+  }
+  b = -1;
+  c = 0;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restrict__ q, float* __restrict__ part,
                                                                 int max_splits, int H, CacheView cache,
@@ -68,16 +114,19 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(const T* __restr
   // query heads): a group with more than 16 heads (R = 32, MQA at 32 heads)
   // takes one workgroup per subset, each reading the group's K/V
   const int nsub = (R + 15) / 16;
-  const int b = blockIdx.x / (G * nsub), g = (blockIdx.x / nsub) % G, hsub = blockIdx.x % nsub;
+  const int gs = blockIdx.x % (G * nsub);
+  const int g = gs / nsub, hsub = gs % nsub;
   const int h0 = g * R + 16 * hsub, RS = min(16, R - 16 * hsub);  // first head, heads in the subset
-  const int split = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int b, split;
+  unit_chunk(batch, blockIdx.x / (G * nsub), lane, b, split);
+  if (b < 0) return;
   const int seq = batch.desc[2 * b];
   const int kv_len = batch.desc[2 * b + 1] + 1;
   const int k_begin = split * kChunkKeys;
   if (k_begin >= kv_len) return;
   const int k_end = min(kv_len, k_begin + kChunkKeys);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g4 = lane >> 4;
   const int HD = H * D;
 
@@ -280,11 +329,16 @@ __global__ __launch_bounds__(256, 3) void attn_decode_wave_kernel(const bf16* __
   // query heads): a group with more than 16 heads (R = 32, MQA at 32 heads)
   // takes one workgroup per subset, each reading the group's K/V
   const int nsub = (R + 15) / 16;
-  const int b = blockIdx.x / (G * nsub), g = (blockIdx.x / nsub) % G, hsub = blockIdx.x % nsub;
+  const int gs = blockIdx.x % (G * nsub);
+  const int g = gs / nsub, hsub = gs % nsub;
   const int h0 = g * R + 16 * hsub, RS = min(16, R - 16 * hsub);  // first head, heads in the subset
-  const int split = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int b, split;
+  unit_chunk(batch, blockIdx.x / (G * nsub), lane, b, split);
+  b = __builtin_amdgcn_readfirstlane(b);
+  split = __builtin_amdgcn_readfirstlane(split);
+  if (b < 0) return;
   const int seq = batch.desc[2 * b];
   const int kv_len = batch.desc[2 * b + 1] + 1;
   if (split * kChunkKeys >= kv_len) return;
@@ -428,8 +482,8 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* _
 
 template <typename T, int D>
 hipError_t launch_split(const void* q, float* part, int max_splits, int H, const CacheView& c, const BatchView& b,
-                        hipStream_t s) {
-  dim3 grid(c.G * ((H / c.G + 15) / 16) * b.batch, max_splits);
+                        int units, hipStream_t s) {
+  dim3 grid(c.G * ((H / c.G + 15) / 16) * units);
   attn_decode_split_kernel<T, D><<<grid, 256, 0, s>>>(reinterpret_cast<const T*>(q), part, max_splits, H, c, b);
   return hipGetLastError();
 }
@@ -446,10 +500,11 @@ hipError_t launch_combine(const float* part, void* attn, int max_splits, int H, 
 int decode_split_keys() { return kChunkKeys; }
 
 hipError_t launch_attn_decode(DType t, const void* q, float* partial, int max_splits, int H, const CacheView& c,
-                              const BatchView& b, hipStream_t s) {
+                              const BatchView& b, int units, hipStream_t s) {
   if (H % c.G != 0 || H / c.G > 32) return hipErrorInvalidValue;
+  if (units <= 0 || units > b.batch * max_splits) return hipErrorInvalidValue;
   if (t == DType::BF16) {
-    dim3 grid(c.G * ((H / c.G + 15) / 16) * b.batch, max_splits);
+    dim3 grid(c.G * ((H / c.G + 15) / 16) * units);
     if (c.D == 128)
       attn_decode_wave_kernel<128><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(q), partial, max_splits, H, c, b);
     else if (c.D == 64)
@@ -458,7 +513,7 @@ hipError_t launch_attn_decode(DType t, const void* q, float* partial, int max_sp
       return hipErrorInvalidValue;
     return hipGetLastError();
   } else {
-    if (c.D == 64) return launch_split<float, 64>(q, partial, max_splits, H, c, b, s);
+    if (c.D == 64) return launch_split<float, 64>(q, partial, max_splits, H, c, b, units, s);
   }
   return hipErrorInvalidValue;
 }

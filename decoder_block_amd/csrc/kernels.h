@@ -95,10 +95,14 @@ hipError_t launch_attn_prefill(DType t, const void* q, void* attn, int H, const 
 
 // Split-K paged decode attention.  partial: [B][H][max_splits][D + 2] fp32
 // holding (running max, sum, unnormalised output) per key chunk; the combine
-// kernel merges the chunks into attn [B][H*D] (bf16 tiled).
+// kernel merges the chunks into attn [B][H*D] (bf16 tiled).  units: the
+// number of (sequence, chunk) work units, sum over b of
+// ceil(kv_len_b / decode_split_keys()) with kv_len_b the length including
+// the new token (the host knows the lengths; the kernel derives each
+// workgroup's unit from the batch descriptor).
 int decode_split_keys();
 hipError_t launch_attn_decode(DType t, const void* q, float* partial, int max_splits, int H,
-                              const CacheView& c, const BatchView& b, hipStream_t s);
+                              const CacheView& c, const BatchView& b, int units, hipStream_t s);
 hipError_t launch_attn_decode_combine(DType t, const float* partial, void* attn, int max_splits,
                                       int H, int D, const BatchView& b, hipStream_t s);
 

@@ -711,12 +711,16 @@ llama_status check_call(const Shape& s, const llama_kv_cache* c, int32_t batch, 
 // (all but the last batch of them launched here; the last rides on the first
 // kernel), and advance the sequence lengths.
 llama_status begin_call(llama_kv_cache* c, int32_t batch, int32_t seq_len, const int32_t* seq_ids, int32_t* desc,
-                        hipStream_t hs, const llk::Upload** last_upload, Uploader* up) {
+                        hipStream_t hs, const llk::Upload** last_upload, Uploader* up, int* attn_units) {
   std::vector<int32_t> start(batch);
   for (int b = 0; b < batch; ++b)
     start[b] = (seq_ids[b] >= 0 && seq_ids[b] < c->max_seqs) ? c->seqs[seq_ids[b]].len : 0;
   llama_status st = reserve(c, batch, seq_ids, seq_len, up);
   if (st != LLAMA_OK) return st;
+  // (sequence, key chunk) work units of the decode attention after this call
+  const int ck = llk::decode_split_keys();
+  *attn_units = 0;
+  for (int b = 0; b < batch; ++b) *attn_units += (start[b] + seq_len + ck - 1) / ck;
   for (int b = 0; b < batch; ++b) {
     up->add(desc, 2 * b, seq_ids[b]);
     up->add(desc, 2 * b + 1, start[b]);
@@ -732,7 +736,7 @@ llama_status begin_call(llama_kv_cache* c, int32_t batch, int32_t seq_len, const
 // go to the pools of `cv`.
 llama_status run_layer(llama_layer* L, const llk::CacheView& cv, const llk::BatchView& bv, int M, const void* x,
                        void* out, DType out_t, char* W, const WsLayout& wl, const llk::Upload* last_upload,
-                       hipStream_t hs, bool decode) {
+                       hipStream_t hs, bool decode, int attn_units) {
   const Shape& s = L->s;
   float* r1 = reinterpret_cast<float*>(W + wl.r1);
   float* r2 = reinterpret_cast<float*>(W + wl.r2);
@@ -783,7 +787,7 @@ llama_status run_layer(llama_layer* L, const llk::CacheView& cv, const llk::Batc
   // attention
   if (decode) {
     const int ms = max_splits_for(s);
-    HIP_TRY(timed(L, K_ATTN_DECODE, hs, [&] { return llk::launch_attn_decode(s.dt, qb, part, ms, s.H, cv, bv, hs); }));
+    HIP_TRY(timed(L, K_ATTN_DECODE, hs, [&] { return llk::launch_attn_decode(s.dt, qb, part, ms, s.H, cv, bv, attn_units, hs); }));
     HIP_TRY(timed(L, K_ATTN_COMBINE, hs,
                   [&] { return llk::launch_attn_decode_combine(s.dt, part, attn, ms, s.H, s.D, bv, hs); }));
   } else {
@@ -858,11 +862,12 @@ llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, int32_t s
   int32_t* desc = reinterpret_cast<int32_t*>(W + wl.desc);
   Uploader up;
   const llk::Upload* last_upload = nullptr;
-  st = begin_call(c, batch, seq_len, seq_ids, desc, hs, &last_upload, &up);
+  int units = 0;
+  st = begin_call(c, batch, seq_len, seq_ids, desc, hs, &last_upload, &up, &units);
   if (st != LLAMA_OK) return st;
   const llk::BatchView bv{desc, batch, seq_len};
   return run_layer(L, cache_view(c), bv, M, x, out, out_dtype == LLAMA_DTYPE_F32 ? DType::F32 : DType::BF16, W, wl,
-                   last_upload, hs, decode);
+                   last_upload, hs, decode, units);
 }
 
 }  // namespace
@@ -922,7 +927,8 @@ llama_status stack_forward(llama_stack* S, llama_kv_cache* c, int32_t batch, int
   int32_t* desc = reinterpret_cast<int32_t*>(W + sw.layer.desc);
   Uploader up;
   const llk::Upload* last_upload = nullptr;
-  st = begin_call(c, batch, seq_len, seq_ids, desc, hs, &last_upload, &up);
+  int units = 0;
+  st = begin_call(c, batch, seq_len, seq_ids, desc, hs, &last_upload, &up, &units);
   if (st != LLAMA_OK) return st;
   const llk::BatchView bv{desc, batch, seq_len};
   // x_{l+1} = layer_l(x_l), held in the layer dtype between layers
@@ -930,7 +936,7 @@ llama_status stack_forward(llama_stack* S, llama_kv_cache* c, int32_t batch, int
   for (int l = 0; l < nl; ++l) {
     void* nxt = W + sw.act[l & 1];
     st = run_layer(S->layers[l], cache_view(c, l), bv, M, cur, nxt, L0->s.dt, W, sw.layer,
-                   l == 0 ? last_upload : nullptr, hs, decode);
+                   l == 0 ? last_upload : nullptr, hs, decode, units);
     if (st != LLAMA_OK) return st;
     cur = nxt;
   }

@@ -27,6 +27,7 @@ static int g_events = 0;
 static int g_uploads = 0;
 struct PackCall { int rows, cols, ldd, row_mul, row_add, head_pairs; bool gamma; };
 static std::vector<PackCall> g_packs;
+static int g_attn_units = -1;  // work units of the last decode-attention launch
 static std::vector<const void*> g_ins;   // x of each first-norm / final-norm launch
 static std::vector<void*> g_outs;        // out of each down-projection launch
 struct FinalCall { const void* gamma; void* y; };
@@ -75,7 +76,9 @@ hipError_t launch_attn_prefill(DType, const void*, void*, int, const CacheView&,
   return hipSuccess;
 }
 int decode_split_keys() { return 1024; }
-hipError_t launch_attn_decode(DType, const void*, float*, int, int, const CacheView&, const BatchView&, hipStream_t) {
+hipError_t launch_attn_decode(DType, const void*, float*, int, int, const CacheView&, const BatchView&, int units,
+                              hipStream_t) {
+  g_attn_units = units;
   g_log.push_back("attn_decode");
   return hipSuccess;
 }
@@ -320,6 +323,7 @@ int main() {
   CHECK(llama_kv_cache_free_blocks(C, &n) == LLAMA_OK && n == NB - 5);
   CHECK(tab[0 * maxb + 2] == 0);  // order[4]
   CHECK(desc[0] == s0 && desc[1] == 32);
+  CHECK(g_attn_units == 1);  // one sequence, 33 keys: one chunk
   CHECK(g_log.size() == 13 * 8 && g_log[2] == "attn_decode" && g_log[3] == "attn_combine");
 
   // per-kernel timing: two events per launch, totals per kernel family
@@ -507,6 +511,7 @@ int main() {
     g_log.clear();
     CHECK(llama_stack_decode(S, C3, 2, sids, x3, y3, LLAMA_DTYPE_F32, ws3, nullptr) == LLAMA_OK);
     CHECK(g_log.size() == NL * 8 + 1 && g_log.back() == "rms_final" && g_log[2] == "attn_decode");
+    CHECK(g_attn_units == 2);  // two sequences of 21 keys
     CHECK(llama_kv_cache_seq_len(C3, sb, &n) == LLAMA_OK && n == 21);
     // per-layer pools: K/V written as [NL, n, G, D] come back per layer, unaliased
     {
