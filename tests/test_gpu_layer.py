@@ -404,3 +404,26 @@ def test_mqa_decode_batch64_full_contexts():
     e = P.assert_close(P.to_np(o), ref, "bf16", "MQA decode B=64")
     print("MQA decode B=64", e)
 
+
+
+# ----------------------------------------------------------------------------
+# bf16 at head_dim 64 (d 2048, 32 query heads) and GQA ratios 2 and 4
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("G", [16, 8])
+def test_bf16_head_dim_64_prefill_and_decode(G):
+    w = synth.scaled(W[3], hidden_size=2048, intermediate_size=5632, num_key_value_heads=G, batch=2, seq_len=300)
+    got, ref, (layer, cache, sids, k_ref, v_ref) = _prefill_case(w, block_seed=G)
+    e = P.assert_close(got, ref, "bf16", f"D=64 R={32 // G} prefill")
+    print("D=64 prefill", G, e)
+    k, v = cache.read(sids[0], 0, w.seq_len)
+    P.assert_close(P.to_np(k), k_ref[0], "bf16", "D=64 cached K")
+    P.assert_close(P.to_np(v), v_ref[0], "bf16", "D=64 cached V")
+    wd = synth.scaled(W[4], hidden_size=2048, intermediate_size=5632, num_key_value_heads=G, batch=4)
+    layer_d, cache_d, sids_d, host, wo = _decode_setup(wd, lens=[1, 17, 1024, 2500], block_seed=G + 1)
+    xt = synth.decode_input(wd, 0)
+    o = layer_d.decode(cache_d, sids_d, xt.cuda())
+    torch.cuda.synchronize()
+    r, _ = oracle.decode_step(_cfg(wd), wo, synth.as_f64(xt), host)
+    e = P.assert_close(P.to_np(o), r, "bf16", f"D=64 R={32 // G} decode")
+    print("D=64 decode", G, e)
