@@ -427,3 +427,27 @@ def test_bf16_head_dim_64_prefill_and_decode(G):
     r, _ = oracle.decode_step(_cfg(wd), wo, synth.as_f64(xt), host)
     e = P.assert_close(P.to_np(o), r, "bf16", f"D=64 R={32 // G} decode")
     print("D=64 decode", G, e)
+
+
+def test_single_token_prefill_and_wide_decode_batch():
+    # a one-token continuation prefill (prefill attention with S = 1) and a
+    # decode batch wider than the few-token GEMM path (160 tokens), both
+    # against the oracle
+    w = synth.scaled(W[3], batch=1, seq_len=120)
+    ws, wo = P.weights_for(w)
+    layer = P.make_layer(w, ws, max_position=w.seq_len + 2)
+    x = synth.layer_input(w)
+    cache = P.make_cache(layer, w, w.seq_len + 1, 1)
+    _, sids = P.gpu_prefill(layer, cache, x[:, :119])
+    one, _ = P.gpu_prefill(layer, cache, x[:, 119:].contiguous(), sids=sids)
+    ref, _, _ = oracle.prefill(_cfg(w), wo, synth.as_f64(x), rows=[119])
+    P.assert_close(P.to_np(one)[:, 0], ref[:, 0], "bf16", "one-token continuation prefill")
+    assert cache.seq_len(sids[0]) == 120
+
+    wd = synth.scaled(W[4], batch=160, ctx_lo=16, ctx_hi=700)
+    layer_d, cache_d, sids_d, host, wo_d = _decode_setup(wd, block_seed=13)
+    xt = synth.decode_input(wd, 0)
+    o = layer_d.decode(cache_d, sids_d, xt.cuda())
+    torch.cuda.synchronize()
+    r, _ = oracle.decode_step(_cfg(wd), wo_d, synth.as_f64(xt), host)
+    P.assert_close(P.to_np(o), r, "bf16", "decode B=160")
