@@ -115,6 +115,8 @@ hipError_t launch_attn_decode_combine(DType t, const float* partial, void* attn,
 hipError_t launch_pack(DType t, const void* src, const void* gamma, void* dst, int rows,
                        int cols, int ldd, int row_mul, int row_add, int head_pairs, hipStream_t s);
 hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s);
+// Every byte of dst[0, bytes) set to `byte`.
+hipError_t launch_fill(void* dst, size_t bytes, uint8_t byte, hipStream_t s);
 // dst[i] = float(src[i]) for n elements of the layer dtype.
 hipError_t launch_to_f32(DType t, const void* src, float* dst, int n, hipStream_t s);
 

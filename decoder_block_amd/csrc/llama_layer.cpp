@@ -175,6 +175,16 @@ bool trace_on() {
   return v == 1;
 }
 
+// LLAMA_LAYER_POISON=1: fill each call's workspace with 0xFF bytes (NaN in
+// fp32 and bf16) before any of its kernels run, so that a kernel reading
+// workspace memory the same call has not written shows up as NaN or changed
+// bits in the outputs (a device-side check for missing writes and races).
+// Read at every call.
+bool poison_on() {
+  const char* e = std::getenv("LLAMA_LAYER_POISON");
+  return e && *e && *e != '0';
+}
+
 #define HIP_TRY(expr)                                                                   \
   do {                                                                                  \
     hipError_t _e = (expr);                                                             \
@@ -860,6 +870,7 @@ llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, int32_t s
   const WsLayout wl = ws_layout(L->s, (size_t)M, (size_t)batch);
   char* W = reinterpret_cast<char*>(workspace);
   int32_t* desc = reinterpret_cast<int32_t*>(W + wl.desc);
+  if (poison_on()) HIP_TRY(llk::launch_fill(W, wl.total, 0xFF, hs));  // before the uploads into it
   Uploader up;
   const llk::Upload* last_upload = nullptr;
   int units = 0;
@@ -925,6 +936,7 @@ llama_status stack_forward(llama_stack* S, llama_kv_cache* c, int32_t batch, int
   const StackWs sw = stack_ws(L0->s, (size_t)M, (size_t)batch);
   char* W = reinterpret_cast<char*>(workspace);
   int32_t* desc = reinterpret_cast<int32_t*>(W + sw.layer.desc);
+  if (poison_on()) HIP_TRY(llk::launch_fill(W, sw.total, 0xFF, hs));  // before the uploads into it
   Uploader up;
   const llk::Upload* last_upload = nullptr;
   int units = 0;

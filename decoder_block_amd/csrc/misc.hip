@@ -31,11 +31,12 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, co
   }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(u32x4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail,
-                                                   int ntail) {
+__global__ __launch_bounds__(256) void fill_kernel(u32x4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail,
+                                                   int ntail, uint32_t byte) {
+  const uint32_t w = byte * 0x01010101u;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
-    p[i] = u32x4{0u, 0u, 0u, 0u};
-  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+    p[i] = u32x4{w, w, w, w};
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = (uint8_t)byte;
 }
 
 template <typename T>
@@ -98,13 +99,15 @@ hipError_t launch_pack(DType t, const void* src, const void* gamma, void* dst, i
   return hipGetLastError();
 }
 
-hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s) {
+hipError_t launch_fill(void* dst, size_t bytes, uint8_t byte, hipStream_t s) {
   const size_t n16 = bytes / 16;
   const int ntail = (int)(bytes % 16);
-  zero_kernel<<<grid_for(n16), 256, 0, s>>>(reinterpret_cast<u32x4*>(dst), n16,
-                                            reinterpret_cast<uint8_t*>(dst) + n16 * 16, ntail);
+  fill_kernel<<<grid_for(n16), 256, 0, s>>>(reinterpret_cast<u32x4*>(dst), n16,
+                                            reinterpret_cast<uint8_t*>(dst) + n16 * 16, ntail, byte);
   return hipGetLastError();
 }
+
+hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s) { return launch_fill(dst, bytes, 0, s); }
 
 hipError_t launch_to_f32(DType t, const void* src, float* dst, int n, hipStream_t s) {
   if (t == DType::BF16)

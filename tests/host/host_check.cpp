@@ -110,6 +110,11 @@ hipError_t launch_to_f32(DType, const void*, float* dst, int n, hipStream_t) {
   for (int i = 0; i < n; ++i) dst[i] = 1.0f;
   return hipSuccess;
 }
+hipError_t launch_fill(void* dst, size_t bytes, uint8_t byte, hipStream_t) {
+  std::memset(dst, byte, bytes);
+  g_log.push_back("fill");
+  return hipSuccess;
+}
 hipError_t launch_zero(void* dst, size_t bytes, hipStream_t) {
   std::memset(dst, 0, bytes);
   return hipSuccess;
@@ -325,6 +330,20 @@ int main() {
   CHECK(desc[0] == s0 && desc[1] == 32);
   CHECK(g_attn_units == 1);  // one sequence, 33 keys: one chunk
   CHECK(g_log.size() == 13 * 8 && g_log[2] == "attn_decode" && g_log[3] == "attn_combine");
+
+  // LLAMA_LAYER_POISON: the workspace is filled before the call's uploads and kernels
+  {
+    setenv("LLAMA_LAYER_POISON", "1", 1);
+    g_log.clear();
+    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+    CHECK(!g_log.empty() && g_log[0] == "fill" && g_log.size() == 9);
+    CHECK(desc[0] == s0 && desc[1] == 33);  // descriptors written after the fill
+    unsetenv("LLAMA_LAYER_POISON");
+    g_log.clear();
+    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+    CHECK(g_log.size() == 8 && g_log[0] == "rms1");
+    CHECK(desc[1] == 34);
+  }
 
   // per-kernel timing: two events per launch, totals per kernel family
   {
