@@ -8,9 +8,11 @@
 // of the batch is read once per KV group, shared by the R = H/G query heads.
 //
 // Split kernel: a workgroup (4 waves) takes one (sequence, group, chunk of
-// 1024 keys) and up to 16 of the group's query heads (two workgroups per
-// chunk at R = 32); each wave walks 32-key steps (two 16-key cache blocks)
-// and runs both products on 16x16 MFMAs with the heads as the 16 columns:
+// 1024 keys) and the group's query heads in 16-column MFMA groups (bf16: one
+// group up to R = 16, two at R = 32, so K and V are read once per KV group
+// either way; fp32: one workgroup per 16 heads); each wave walks its keys
+// block by block and runs both products on
+// 16x16 MFMAs with the heads as the 16 columns:
 //   S^T [16 keys x heads] = K_block [16 x D] * Q^T   (K loaded straight from HBM)
 //   O^T [D x heads]      += V_block^T [D x 32 keys] * P^T
 // V is kept transposed per block in the cache, so the A operand of the second
@@ -318,20 +320,21 @@ DEVI f32x4 mfma16x16x16(f32x4 c, u32x2 a, u32x2 b) {
                                                     0);
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 3) void attn_decode_wave_kernel(const bf16* __restrict__ q, float* __restrict__ part,
-                                                               int max_splits, int H, CacheView cache,
-                                                               BatchView batch) {
-  __shared__ float sm[4][16][D + 2];
+// NG head groups of 16 per workgroup: NG = 2 serves the 32 query heads of an
+// MQA group (R = 32) with one read of its K/V instead of one per 16 heads.
+template <int D, int NG>
+__global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_decode_wave_kernel(
+    const bf16* __restrict__ q, float* __restrict__ part, int max_splits, int H, CacheView cache, BatchView batch) {
+  constexpr int HW = 16 * NG;  // heads per workgroup
+  __shared__ float sm[4][HW][D + 2];
   const int G = cache.G;
   const int R = H / G;
-  // workgroup -> (sequence b, KV group g, 16-head subset sub of the group's R
-  // query heads): a group with more than 16 heads (R = 32, MQA at 32 heads)
-  // takes one workgroup per subset, each reading the group's K/V
-  const int nsub = (R + 15) / 16;
+  // workgroup -> (sequence b, KV group g, subset hsub of up to HW of the
+  // group's R query heads); each subset's workgroup reads the group's K/V
+  const int nsub = (R + HW - 1) / HW;
   const int gs = blockIdx.x % (G * nsub);
   const int g = gs / nsub, hsub = gs % nsub;
-  const int h0 = g * R + 16 * hsub, RS = min(16, R - 16 * hsub);  // first head, heads in the subset
+  const int h0 = g * R + HW * hsub, RS = min(HW, R - HW * hsub);  // first head, heads in the subset
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int b, split;
@@ -347,53 +350,63 @@ __global__ __launch_bounds__(256, 3) void attn_decode_wave_kernel(const bf16* __
   const int nblk = (nkeys + 15) >> 4;
 
   const int c16 = lane & 15, g4 = lane >> 4;
-  bf16x8 qf[D / 32];
-  {
-    const bf16* qp = q + (size_t)b * H * D + (size_t)(h0 + c16) * D;
+  bf16x8 qf[NG][D / 32];
 #pragma unroll
-    for (int s = 0; s < D / 32; ++s) qf[s] = c16 < RS ? load_chunk<bf16>(qp + (4 * s + g4) * 8) : zero_chunk<bf16>();
+  for (int ng = 0; ng < NG; ++ng) {
+    const int hc = 16 * ng + c16;
+    const bf16* qp = q + (size_t)b * H * D + (size_t)(h0 + hc) * D;
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s)
+      qf[ng][s] = hc < RS ? load_chunk<bf16>(qp + (4 * s + g4) * 8) : zero_chunk<bf16>();
   }
   const int32_t* btab = cache.block_table + (size_t)seq * cache.max_blocks + (k_begin >> 4);
   const bf16* kpool = reinterpret_cast<const bf16*>(cache.k_pool);
   const bf16* vpool = reinterpret_cast<const bf16*>(cache.v_pool);
 
   // q arrives multiplied by log2(e)/sqrt(D) (QKV epilogue): scores are in exp2 units
-  constexpr float scale = 1.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4 o[D / 16];
+  float m_run[NG], l_run[NG];
+  f32x4 o[NG][D / 16];
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ng = 0; ng < NG; ++ng) {
+    m_run[ng] = -INFINITY;
+    l_run[ng] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) o[ng][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   auto compute = [&](KV16<D>& r, int i) {
     const int key0 = 16 * i;  // within the wave's range
-    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s) sc = mfma16_chunk(sc, r.k[s], qf[s]);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float sv = key0 + 4 * g4 + e < nkeys ? sc[e] * scale : -INFINITY;
-      sc[e] = sv;
-      mx = fmaxf(mx, sv);
-    }
-    mx = fmaxf(mx, shfl_xor(mx, 16));
-    mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2(m_run - m_new);
-    float p[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - m_new);
-    l_run = l_run * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-    m_run = m_new;
     if (key0 + 16 > nkeys) {  // keys past the end may hold stale data: zero their values
       const int nvalid = nkeys - (key0 + 4 * g4);
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) r.v[db] = keep_first(r.v[db], nvalid);
     }
-    const bf16x4 pb = {from_f32<bf16>(p[0]), from_f32<bf16>(p[1]), from_f32<bf16>(p[2]), from_f32<bf16>(p[3])};
-    const u32x2 pw = __builtin_bit_cast(u32x2, pb);
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) o[db] = mfma16x16x16(o[db] * alpha, r.v[db], pw);
+    for (int ng = 0; ng < NG; ++ng) {
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < D / 32; ++s) sc = mfma16_chunk(sc, r.k[s], qf[ng][s]);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float sv = key0 + 4 * g4 + e < nkeys ? sc[e] : -INFINITY;
+        sc[e] = sv;
+        mx = fmaxf(mx, sv);
+      }
+      mx = fmaxf(mx, shfl_xor(mx, 16));
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run[ng], mx);
+      const float alpha = fast_exp2(m_run[ng] - m_new);
+      float p[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - m_new);
+      l_run[ng] = l_run[ng] * alpha + (p[0] + p[1]) + (p[2] + p[3]);
+      m_run[ng] = m_new;
+      const bf16x4 pb = {from_f32<bf16>(p[0]), from_f32<bf16>(p[1]), from_f32<bf16>(p[2]), from_f32<bf16>(p[3])};
+      const u32x2 pw = __builtin_bit_cast(u32x2, pb);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) o[ng][db] = mfma16x16x16(o[ng][db] * alpha, r.v[db], pw);
+    }
   };
 
   // Two register buffers; every iteration issues the same loads (blocks past
@@ -414,36 +427,45 @@ __global__ __launch_bounds__(256, 3) void attn_decode_wave_kernel(const bf16* __
   }
 
   // ---- merge the four waves (a wave without keys has m = -inf, l = 0, o = 0) ----
-  l_run += shfl_xor(l_run, 16);
-  l_run += shfl_xor(l_run, 32);
 #pragma unroll
-  for (int db = 0; db < D / 16; ++db)
+  for (int ng = 0; ng < NG; ++ng) {
+    float l = l_run[ng];
+    l += shfl_xor(l, 16);
+    l += shfl_xor(l, 32);
+    const int hc = 16 * ng + c16;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm[wave][c16][2 + 16 * db + 4 * g4 + e] = o[db][e];
-  if (g4 == 0) {
-    sm[wave][c16][0] = m_run;
-    sm[wave][c16][1] = l_run;
+    for (int db = 0; db < D / 16; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sm[wave][hc][2 + 16 * db + 4 * g4 + e] = o[ng][db][e];
+    if (g4 == 0) {
+      sm[wave][hc][0] = m_run[ng];
+      sm[wave][hc][1] = l;
+    }
   }
   __syncthreads();
-  const int hh = tid >> 4, sub = tid & 15;
-  if (hh >= RS) return;
-  float M = -INFINITY;
+  const int sub = tid & 15;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][hh][0]);
-  float f[4];
+  for (int ng = 0; ng < NG; ++ng) {
+    const int hh = 16 * ng + (tid >> 4);
+    if (hh >= RS) continue;
+    float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) f[w] = fast_exp2(sm[w][hh][0] - M);  // waves without keys: exp2(-inf) = 0
-  float* dst = part + (((size_t)b * H + h0 + hh) * max_splits + split) * (D + 2);
-  for (int x = sub; x < D + 2; x += 16) {
-    float v;
-    if (x == 0) {
-      v = M;
-    } else {
-      v = 0.f;
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][hh][0]);
+    float f[4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) v += f[w] * sm[w][hh][x];
+    for (int w = 0; w < 4; ++w) f[w] = fast_exp2(sm[w][hh][0] - M);  // waves without keys: exp2(-inf) = 0
+    float* dst = part + (((size_t)b * H + h0 + hh) * max_splits + split) * (D + 2);
+    for (int x = sub; x < D + 2; x += 16) {
+      float v;
+      if (x == 0) {
+        v = M;
+      } else {
+        v = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) v += f[w] * sm[w][hh][x];
+      }
+      dst[x] = v;
     }
-    dst[x] = v;
   }
 }
 
@@ -504,13 +526,24 @@ hipError_t launch_attn_decode(DType t, const void* q, float* partial, int max_sp
   if (H % c.G != 0 || H / c.G > 32) return hipErrorInvalidValue;
   if (units <= 0 || units > b.batch * max_splits) return hipErrorInvalidValue;
   if (t == DType::BF16) {
-    dim3 grid(c.G * ((H / c.G + 15) / 16) * units);
-    if (c.D == 128)
-      attn_decode_wave_kernel<128><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(q), partial, max_splits, H, c, b);
-    else if (c.D == 64)
-      attn_decode_wave_kernel<64><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(q), partial, max_splits, H, c, b);
-    else
-      return hipErrorInvalidValue;
+    const bf16* qb = reinterpret_cast<const bf16*>(q);
+    if (H / c.G > 16) {  // 32 heads per group: both 16-head halves in one workgroup
+      dim3 grid(c.G * ((H / c.G + 31) / 32) * units);
+      if (c.D == 128)
+        attn_decode_wave_kernel<128, 2><<<grid, 256, 0, s>>>(qb, partial, max_splits, H, c, b);
+      else if (c.D == 64)
+        attn_decode_wave_kernel<64, 2><<<grid, 256, 0, s>>>(qb, partial, max_splits, H, c, b);
+      else
+        return hipErrorInvalidValue;
+    } else {
+      dim3 grid(c.G * units);
+      if (c.D == 128)
+        attn_decode_wave_kernel<128, 1><<<grid, 256, 0, s>>>(qb, partial, max_splits, H, c, b);
+      else if (c.D == 64)
+        attn_decode_wave_kernel<64, 1><<<grid, 256, 0, s>>>(qb, partial, max_splits, H, c, b);
+      else
+        return hipErrorInvalidValue;
+    }
     return hipGetLastError();
   } else {
     if (c.D == 64) return launch_split<float, 64>(q, partial, max_splits, H, c, b, units, s);
