@@ -307,6 +307,20 @@ def llama_layer_profile_read(layer, reset: bool = True) -> dict:
 _TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
+def _check_tensor(t: torch.Tensor, what: str, dtype, device, shape=None):
+    """The C ABI takes raw pointers: reject tensors it would misread."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{what}: on {t.device}, the layer is on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def _dev_bytes(n: int, device) -> torch.Tensor:
     # 256-byte aligned by the caching allocator (it aligns blocks to 512 bytes)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
@@ -341,8 +355,10 @@ class DecoderLayer:
     def prefill(self, cache: "PagedKVCache", seq_ids, x: torch.Tensor, out_dtype="f32", out=None, stream=None):
         B, S, d = x.shape
         odt = _TORCH_DT[out_dtype]
+        _check_tensor(x, "x", self.tdtype, self.device, (B, S, self.cfg.hidden_size))
         if out is None:
             out = torch.empty((B, S, d), dtype=odt, device=self.device)
+        _check_tensor(out, "out", odt, self.device, (B, S, d))
         ws = self.workspace(B * S, B)
         llama_layer_prefill(self.handle, cache.handle, B, S, list(seq_ids), x, out,
                             LLAMA_DTYPE_F32 if out_dtype == "f32" else LLAMA_DTYPE_BF16, ws, stream)
@@ -351,8 +367,10 @@ class DecoderLayer:
     def decode(self, cache: "PagedKVCache", seq_ids, x: torch.Tensor, out_dtype="f32", out=None, stream=None):
         B, d = x.shape
         odt = _TORCH_DT[out_dtype]
+        _check_tensor(x, "x", self.tdtype, self.device, (B, self.cfg.hidden_size))
         if out is None:
             out = torch.empty((B, d), dtype=odt, device=self.device)
+        _check_tensor(out, "out", odt, self.device, (B, d))
         ws = self.workspace(B, B)
         llama_layer_decode(self.handle, cache.handle, B, list(seq_ids), x, out,
                            LLAMA_DTYPE_F32 if out_dtype == "f32" else LLAMA_DTYPE_BF16, ws, stream)
@@ -397,7 +415,12 @@ class PagedKVCache:
     def write(self, sid: int, k: torch.Tensor, v: torch.Tensor, stream=None):
         """k, v: [n, G, D] (one layer) or [n_layers, n, G, D]."""
         n = k.shape[0] if self.n_layers == 1 and k.dim() == 3 else k.shape[1]
-        llama_kv_cache_write(self.handle, sid, n, k.contiguous(), v.contiguous(), stream)
+        G, D = self.layer.cfg.num_key_value_heads, self.layer.cfg.hidden_size // self.layer.cfg.num_attention_heads
+        shape = (n, G, D) if self.n_layers == 1 and k.dim() == 3 else (self.n_layers, n, G, D)
+        k, v = k.contiguous(), v.contiguous()
+        _check_tensor(k, "k", self.layer.tdtype, self.layer.device, shape)
+        _check_tensor(v, "v", self.layer.tdtype, self.layer.device, shape)
+        llama_kv_cache_write(self.handle, sid, n, k, v, stream)
 
     def read(self, sid: int, start: int, n: int):
         """[n, G, D] K and V (one layer) or [n_layers, n, G, D]."""
@@ -443,8 +466,11 @@ class DecoderStack:
 
     def prefill(self, cache: PagedKVCache, seq_ids, x: torch.Tensor, out_dtype="f32", out=None, stream=None):
         B, S, d = x.shape
+        l0 = self.layers[0]
+        _check_tensor(x, "x", l0.tdtype, self.device, (B, S, l0.cfg.hidden_size))
         if out is None:
             out = torch.empty((B, S, d), dtype=_TORCH_DT[out_dtype], device=self.device)
+        _check_tensor(out, "out", _TORCH_DT[out_dtype], self.device, (B, S, d))
         ws = self.workspace(B * S, B)
         llama_stack_prefill(self.handle, cache.handle, B, S, list(seq_ids), x, out,
                             LLAMA_DTYPE_F32 if out_dtype == "f32" else LLAMA_DTYPE_BF16, ws, stream)
@@ -452,8 +478,11 @@ class DecoderStack:
 
     def decode(self, cache: PagedKVCache, seq_ids, x: torch.Tensor, out_dtype="f32", out=None, stream=None):
         B, d = x.shape
+        l0 = self.layers[0]
+        _check_tensor(x, "x", l0.tdtype, self.device, (B, l0.cfg.hidden_size))
         if out is None:
             out = torch.empty((B, d), dtype=_TORCH_DT[out_dtype], device=self.device)
+        _check_tensor(out, "out", _TORCH_DT[out_dtype], self.device, (B, d))
         ws = self.workspace(B, B)
         llama_stack_decode(self.handle, cache.handle, B, list(seq_ids), x, out,
                            LLAMA_DTYPE_F32 if out_dtype == "f32" else LLAMA_DTYPE_BF16, ws, stream)

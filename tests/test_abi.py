@@ -119,6 +119,25 @@ def test_forward_rejects_null_handles(L):
     assert lib.llama_layer_decode(None, None, 1, ids, None, None, 0, None, None) == -1
 
 
+def test_binding_rejects_tensors_the_abi_would_misread(L):
+    # The binding passes raw pointers; it must refuse what the pointer alone
+    # cannot describe (CPU tensors stand in for device tensors here).
+    import torch
+    dev = torch.device("cpu")
+    x = torch.zeros(2, 3, 8, dtype=torch.bfloat16)
+    L._check_tensor(x, "x", torch.bfloat16, dev, (2, 3, 8))
+    with pytest.raises(ValueError, match="contiguous"):
+        L._check_tensor(x.transpose(0, 1), "x", torch.bfloat16, dev, None)
+    with pytest.raises(ValueError, match="dtype"):
+        L._check_tensor(x.float(), "x", torch.bfloat16, dev, (2, 3, 8))
+    with pytest.raises(ValueError, match="shape"):
+        L._check_tensor(x, "x", torch.bfloat16, dev, (2, 3, 16))
+    with pytest.raises(ValueError, match="on cpu"):
+        L._check_tensor(x, "x", torch.bfloat16, torch.device("meta"), (2, 3, 8))
+    with pytest.raises(TypeError):
+        L._check_tensor([0], "x", torch.bfloat16, dev)
+
+
 def test_host_runtime_under_asan_ubsan():
     """Builds the host runtime with stub kernels under ASan/UBSan and runs its checks."""
     from decoder_block_amd import build
