@@ -311,7 +311,7 @@ def _check_tensor(t: torch.Tensor, what: str, dtype, device, shape=None):
     """The C ABI takes raw pointers: reject tensors it would misread."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{what}: expected a torch.Tensor")
-    if t.device != device:
+    if t.device.type != device.type or (device.index is not None and t.device.index != device.index):
         raise ValueError(f"{what}: on {t.device}, the layer is on {device}")
     if t.dtype != dtype:
         raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
@@ -333,6 +333,8 @@ class DecoderLayer:
         self.dtype = dtype
         self.tdtype = _TORCH_DT[dtype]
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.cfg = make_config(config["hidden_size"], config["intermediate_size"],
                                config["num_attention_heads"], config["num_key_value_heads"],
                                config["rms_norm_eps"], config["rope_theta"], max_position, dtype,

@@ -126,6 +126,9 @@ def test_binding_rejects_tensors_the_abi_would_misread(L):
     dev = torch.device("cpu")
     x = torch.zeros(2, 3, 8, dtype=torch.bfloat16)
     L._check_tensor(x, "x", torch.bfloat16, dev, (2, 3, 8))
+    # a device without an index accepts any index of its type
+    assert torch.device("cuda").index is None
+    L._check_tensor(torch.zeros(2, device="meta"), "x", torch.float32, torch.device("meta"), (2,))
     with pytest.raises(ValueError, match="contiguous"):
         L._check_tensor(x.transpose(0, 1), "x", torch.bfloat16, dev, None)
     with pytest.raises(ValueError, match="dtype"):
