@@ -479,18 +479,33 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* _
   const int kv_len = batch.desc[2 * b + 1] + 1;
   const int ns = (kv_len + kChunkKeys - 1) / kChunkKeys;
   const float* p = part + (size_t)bh * max_splits * (D + 2);
+  // The splits' maxima and sums are fetched one split per lane, all at once,
+  // so the pass costs two rounds of load latency, not two per split.
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, p[s * (D + 2)]);
+  for (int s0 = 0; s0 < ns; s0 += 64)
+    if (s0 + lane < ns) M = fmaxf(M, p[(s0 + lane) * (D + 2)]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor(M, m));
   float L = 0.f;
   float acc[D / 64];
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float* ps = p + s * (D + 2);
-    const float f = exp2f(ps[0] - M);
-    L += f * ps[1];
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int n = min(64, ns - s0);
+    float f_l = 0.f, l_l = 0.f;
+    if (lane < n) {
+      f_l = exp2f(p[(s0 + lane) * (D + 2)] - M);
+      l_l = p[(s0 + lane) * (D + 2) + 1];
+    }
+    // splits added in order (the same sums whatever the lane count)
+#pragma unroll 4
+    for (int i = 0; i < n; ++i) {
+      const float* ps = p + (s0 + i) * (D + 2);
+      const float f = __shfl(f_l, i, 64);
+      L += f * __shfl(l_l, i, 64);
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) acc[e] += f * ps[2 + lane + 64 * e];
+      for (int e = 0; e < D / 64; ++e) acc[e] += f * ps[2 + lane + 64 * e];
+    }
   }
   const float inv = 1.f / L;
 #pragma unroll

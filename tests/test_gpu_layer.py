@@ -105,9 +105,9 @@ def test_bf16_prefill_full_size_sampled_rows(wid, n_random, edge):
 # batched decode over a paged cache pre-filled with N(0,1) keys/values
 # ----------------------------------------------------------------------------
 
-def _decode_setup(w, n_seqs=None, lens=None, block_seed=None):
+def _decode_setup(w, n_seqs=None, lens=None, block_seed=None, max_position=None):
     ws, wo = P.weights_for(w)
-    layer = P.make_layer(w, ws)
+    layer = P.make_layer(w, ws, max_position)
     lens = synth.context_lengths(w) if lens is None else np.asarray(lens)
     B = len(lens)
     nb = int(sum((l + w.decode_steps + 15) // 16 for l in lens))
@@ -152,6 +152,21 @@ def test_decode_ragged_lengths_and_group_ratios():
         torch.cuda.synchronize()
         ref, _ = oracle.decode_step(_cfg(w), wo, synth.as_f64(xt), host)
         P.assert_close(P.to_np(o), ref, "bf16", f"decode G={w.num_key_value_heads}")
+
+
+@pytest.mark.parametrize("wid", [1, 4])
+def test_decode_context_past_64_key_chunks(wid):
+    # 70000 keys: more key chunks than a wave has lanes, so the combine pass
+    # takes its chunk statistics in two rounds; a 3-key sequence rides along
+    w = synth.scaled(W[wid], batch=2)
+    lens = [70000, 3]
+    layer, cache, sids, host, wo = _decode_setup(w, lens=lens, block_seed=11, max_position=70008)
+    xt = synth.decode_input(w, 0)
+    o = layer.decode(cache, sids, xt.cuda())
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode_step(_cfg(w), wo, synth.as_f64(xt), host)
+    e = P.assert_close(P.to_np(o), ref, w.dtype, "decode past 64 chunks")
+    print("decode 70000 keys", e)
 
 
 # ----------------------------------------------------------------------------
