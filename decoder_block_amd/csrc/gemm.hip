@@ -26,9 +26,10 @@
 // keeps the tiles that share weight panels on one XCD (8 XCDs, each with its
 // own L2).
 //
-// bf16 operands (packed weights and the activations the layer writes for a
-// GEMM) are stored in 256-row x 32-column tiles (tiled_off): a stage of a tile
-// is then one contiguous piece of 64-byte rows, and its DMAs fetch whole
+// bf16 operands are stored in 64-byte rows of 32 columns: the activations the
+// layer writes for a GEMM in 256-row x 32-column tiles (tiled_off), the packed
+// weights K block first (wtiled_off, w_rows rows per K block).  A stage of a
+// tile is then one contiguous piece of 64-byte rows, and its DMAs fetch whole
 // 128-byte lines.  With row-major operands a 32-deep stage touches half of
 // every line of its rows, and the DMA stream into LDS was measured at about
 // 60% of the rate for whole lines; that stream set the GEMMs' speed.
@@ -216,9 +217,10 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   // lane loads exactly that chunk (the swizzle is its own inverse).  Rows of X
   // past M fall outside the buffer's range and arrive as zeros.
   constexpr int ES = (int)sizeof(T);
-  // bf16 operands are tiled: a stage of BN (BM) rows is one contiguous piece
-  // of 64-byte rows inside a 256 x 32 tile, the next stage 16 KB further.
-  // fp32 operands are row-major with pitch K (W) and ldx (X).
+  // bf16 operands: a stage of BN (BM) rows is one contiguous piece of 64-byte
+  // rows, the next stage w_rows * 64 bytes further for W (K-block-major) and
+  // 16 KB further for X (256 x 32 tiles).  fp32 operands are row-major with
+  // pitch K (W) and ldx (X).
   constexpr bool TILED = sizeof(T) == 2;
   int vW[C::LW], vX[C::LX];
 #pragma unroll
@@ -233,8 +235,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
     const int row = slot >> 2, c = (slot & 3) ^ ((row >> 2) & 3);
     vX[i] = TILED ? row * 64 + c * 16 : (row * a.ldx + c * Chunk<T>::N) * ES;
   }
-  const char* Wt = reinterpret_cast<const char*>(a.W) +
-                   (TILED ? tiled_off(n0, 0, a.K) * ES : (size_t)n0 * a.K * ES);
+  const char* Wt = reinterpret_cast<const char*>(a.W) + (TILED ? (size_t)n0 * 64 : (size_t)n0 * a.K * ES);
   const char* Xt = reinterpret_cast<const char*>(a.X) +
                    (TILED ? tiled_off(m0, 0, a.K) * ES : (size_t)m0 * a.ldx * ES);
   // bytes of X from the tile's first row to the end of the matrix (< 2^31 for
@@ -243,7 +244,8 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   const uint64_t xb = TILED ? (uint64_t)C::BM * 64 : (uint64_t)(a.M - m0) * (uint64_t)a.ldx * ES;
   const int x_bytes = __builtin_amdgcn_readfirstlane((int)(xb < 0x7fffffffull ? xb : 0x7fffffffull));
   const int nk = a.K / C::BK;
-  constexpr int STAGE_BYTES = TILED ? kTileElems * 2 : C::BK * ES;  // distance between stages
+  constexpr int STAGE_BYTES = TILED ? kTileElems * 2 : C::BK * ES;  // distance between X stages
+  const size_t w_stage = TILED ? (size_t)a.w_rows * 64 : (size_t)STAGE_BYTES;  // ... and W stages
 
   auto slot_of = [&](auto s_) -> u32x4* {
     constexpr int S = decltype(s_)::value & 3;
@@ -258,7 +260,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
   auto issue = [&](int kt, u32x4* L) {
     const bool live = kt < nk;
     const int kb = live ? kt * STAGE_BYTES : 0;
-    const i32x4 rW = make_rsrc(Wt + kb, live ? (TILED ? (uint32_t)C::BN * 64 : 0x7fffffffu) : 0u);
+    const i32x4 rW = make_rsrc(Wt + (live ? kt * w_stage : 0), live ? (TILED ? (uint32_t)C::BN * 64 : 0x7fffffffu) : 0u);
     const i32x4 rX = make_rsrc(Xt + kb, live ? (uint32_t)(TILED ? x_bytes : x_bytes - kb) : 0u);
 #pragma unroll
     for (int i = 0; i < C::LW; ++i) buf_dma16_async(rW, L + (wave * C::LW + i) * 64, vW[i]);
@@ -386,9 +388,10 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = wave & 1, wm = wave >> 1;
 
-  // W and X are tiled (256 x 32 tiles): the tile's stage kt is one 16 KB piece
-  // of 64-byte rows for W and one for X, so every DMA fetches whole cache lines.
-  // A lane's 16 bytes sit at the same offset inside every stage.
+  // The tile's stage kt is one 16 KB piece of 64-byte rows for W (K-block-major,
+  // stages w_rows * 64 bytes apart) and one for X (256 x 32 tiles, 16 KB apart),
+  // so every DMA fetches whole cache lines.  A lane's 16 bytes sit at the same
+  // offset inside every stage.
   static_assert(C::BK == kTileCols, "one tile column block per stage");
   constexpr int STAGE_BYTES = kTileElems * 2;
   int voff[C::PER];
@@ -399,15 +402,16 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
     const int c = C::swz(row, slot % C::CPR) - row * C::CPR;
     voff[i] = (row < C::BN ? row : row - C::BN) * 64 + 16 * c;
   }
-  const char* Wt = reinterpret_cast<const char*>(a.W) + tiled_off(n0, 0, a.K) * 2;
+  const char* Wt = reinterpret_cast<const char*>(a.W) + (size_t)n0 * 64;
   const char* Xt = reinterpret_cast<const char*>(a.X) + tiled_off(m0, 0, a.K) * 2;
+  const size_t w_stage = (size_t)a.w_rows * 64;
   const int nk = a.K / C::BK;
   const uint32_t ring_base = lds_address(ring);
 
   // stages past the end get an empty range: no memory moves, same DMA count
   auto rsrc_w = [&](int kt) {
     const bool live = kt < nk;
-    return make_rsrc(Wt + (live ? kt * STAGE_BYTES : 0), live ? (uint32_t)STAGE_BYTES : 0u);
+    return make_rsrc(Wt + (live ? kt * w_stage : 0), live ? (uint32_t)STAGE_BYTES : 0u);
   };
   auto rsrc_x = [&](int kt) {
     const bool live = kt < nk;
@@ -797,14 +801,17 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmArgs a, int KS)
   const int s_beg = nk * ks / KS, s_end = nk * (ks + 1) / KS;
   const int ns = s_end - s_beg;
 
-  // W and X are tiled (256 x 32 tiles): a 64-deep stage of 64 rows is two
-  // contiguous 4 KB pieces, one in each of two consecutive tile column blocks
-  // (16 KB apart).  X rows past M are padding rows of the tile (never stored).
+  // A 64-deep stage of 64 rows is two contiguous 4 KB pieces per operand, one
+  // in each of two consecutive 32-column K blocks: w_rows * 64 bytes apart for
+  // W (K-block-major), 16 KB apart for X (256 x 32 tiles).  X rows past M are
+  // padding rows of the tile (never stored).
   // DMA i of this thread: chunk slot (wave * PER + i) * 64 + lane of a stage
-  const char* Wt = reinterpret_cast<const char*>(a.W) + tiled_off(n0, s_beg * 64, a.K) * 2;
+  const int wkb = a.w_rows * 64;  // bytes between W K blocks
+  const char* Wt = reinterpret_cast<const char*>(a.W) + (size_t)s_beg * 2 * wkb + (size_t)n0 * 64;
   const char* Xt = reinterpret_cast<const char*>(a.X) + tiled_off(m0, s_beg * 64, a.K) * 2;
-  constexpr int STAGE_BYTES = 2 * kTileElems * 2;
-  constexpr uint32_t RANGE = kTileElems * 2 + 64 * 64;  // both 4 KB pieces
+  constexpr int X_STAGE = 2 * kTileElems * 2;
+  const uint32_t W_RANGE = (uint32_t)wkb + 64 * 64;             // both 4 KB pieces
+  constexpr uint32_t X_RANGE = kTileElems * 2 + 64 * 64;
   // DMA group q = wave * PER + i covers rows 8q .. 8q + 7: W rows for q < 8,
   // X rows after (wave-uniform, so the descriptor choice stays scalar)
   int voff[C::PER];
@@ -812,14 +819,14 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(GemmArgs a, int KS)
   for (int i = 0; i < C::PER; ++i) {
     const int slot = (wave * C::PER + i) * 64 + lane;
     const int row = slot / C::CPR, c = (slot % C::CPR) ^ (row & 7);
-    voff[i] = (c >> 2) * kTileElems * 2 + (row & 63) * 64 + (c & 3) * 16;
+    const bool is_x = wave * C::PER + i >= 8;
+    voff[i] = (c >> 2) * (is_x ? kTileElems * 2 : wkb) + (row & 63) * 64 + (c & 3) * 16;
   }
   const uint32_t ring_base = lds_address(ring);
   auto issue = [&](int st) {
     const bool live = st < ns;
-    const int kb = live ? st * STAGE_BYTES : 0;
-    const i32x4 rW = make_rsrc(Wt + kb, live ? RANGE : 0u);
-    const i32x4 rX = make_rsrc(Xt + kb, live ? RANGE : 0u);
+    const i32x4 rW = make_rsrc(Wt + (live ? (size_t)st * 2 * wkb : 0), live ? W_RANGE : 0u);
+    const i32x4 rX = make_rsrc(Xt + (live ? st * X_STAGE : 0), live ? X_RANGE : 0u);
     const uint32_t slot_base = ring_base + (uint32_t)((st % C::NSL) * C::SLOT * 16);
 #pragma unroll
     for (int i = 0; i < C::PER; ++i)
@@ -936,6 +943,7 @@ size_t skinny_partial_bytes(int M, int N, int K) {
 
 hipError_t launch_gemm(DType t, GemmTile tile, const GemmArgs& a, hipStream_t s) {
   if (t == DType::BF16) {
+    if (a.w_rows < a.N || a.w_rows % kTileRows != 0) return hipErrorInvalidValue;  // K-block stride of W
     if (tile == GemmTile::SKINNY) return launch_skinny(a, s);
     return tile == GemmTile::LARGE ? launch_big(a, s) : launch_cfg<bf16, SmallBF>(a, s);
   }

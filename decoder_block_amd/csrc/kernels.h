@@ -32,11 +32,12 @@ struct CacheView {
 
 enum class Epi : int { QKV = 0, RESID_H = 1, SWIGLU = 2, RESID_OUT = 3 };
 
-// bf16 operands are stored in 256 x 32 tiles (tiled_off in common.h): the
-// packed weights with N rounded up to 256 rows, the activations with M rounded
-// up to 256 rows.  fp32 operands are row-major.
+// bf16 activations are stored in 256 x 32 tiles (tiled_off in common.h) with M
+// rounded up to 256 rows; bf16 packed weights K block first (wtiled_off) with
+// N rounded up to 256 rows (w_rows).  fp32 operands are row-major.
 struct GemmArgs {
-  const void* W;  // packed weights [N][K] (features x K): bf16 tiled, fp32 row-major
+  const void* W;  // packed weights [N][K] (features x K): bf16 K-block-major (wtiled_off), fp32 row-major
+  int w_rows;     // bf16 W: its padded row count, so K block kb starts at byte kb * w_rows * 64
   const void* X;  // activations [M][K]: bf16 tiled; fp32 row-major with pitch ldx
   int M, N, K, ldx;
   Epi epi;
@@ -107,13 +108,14 @@ hipError_t launch_attn_decode_combine(DType t, const float* partial, void* attn,
                                       int H, int D, const BatchView& b, hipStream_t s);
 
 // Weight packing.  dst[r][c] = src[r][c] * (gamma ? gamma[c] : 1) for r < rows,
-// c < cols, with ldd columns (bf16: tiled, fp32: row-major); the caller zeroes
+// c < cols (bf16: K-block-major over drows destination rows, wtiled_off; fp32:
+// row-major with ldd columns); the caller zeroes
 // the buffer first, so padded rows and columns stay zero.  Row r of the source
 // lands at dst row (r' * row_mul + row_add), where r' = r, or with head_pairs
 // = D > 0 the rows of each D-row head reordered so that rows w and w + D/2
 // become adjacent: w < D/2 -> 2w, w >= D/2 -> 2(w - D/2) + 1.
 hipError_t launch_pack(DType t, const void* src, const void* gamma, void* dst, int rows,
-                       int cols, int ldd, int row_mul, int row_add, int head_pairs, hipStream_t s);
+                       int cols, int ldd, int drows, int row_mul, int row_add, int head_pairs, hipStream_t s);
 hipError_t launch_zero(void* dst, size_t bytes, hipStream_t s);
 // Every byte of dst[0, bytes) set to `byte`.
 hipError_t launch_fill(void* dst, size_t bytes, uint8_t byte, hipStream_t s);

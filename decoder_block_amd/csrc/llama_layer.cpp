@@ -457,20 +457,20 @@ llama_status llama_layer_create(const llama_layer_config* cfg, const llama_layer
   // form; the QKV epilogue writes each result back to its own position.
   const int rp = s.rope_half ? s.D : 0;
   if (e == hipSuccess)
-    e = llk::launch_pack(s.dt, w->q_proj, w->input_layernorm, P + L->pl.qkv, s.HD, s.d, s.d, 1, 0, rp, hs);
+    e = llk::launch_pack(s.dt, w->q_proj, w->input_layernorm, P + L->pl.qkv, s.HD, s.d, s.d, s.NQKV_pad, 1, 0, rp, hs);
   if (e == hipSuccess)
-    e = llk::launch_pack(s.dt, w->k_proj, w->input_layernorm, P + L->pl.qkv, s.KD, s.d, s.d, 1, s.HD, rp, hs);
+    e = llk::launch_pack(s.dt, w->k_proj, w->input_layernorm, P + L->pl.qkv, s.KD, s.d, s.d, s.NQKV_pad, 1, s.HD, rp, hs);
   if (e == hipSuccess)
-    e = llk::launch_pack(s.dt, w->v_proj, w->input_layernorm, P + L->pl.qkv, s.KD, s.d, s.d, 1, s.HD + s.KD, 0, hs);
-  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->o_proj, nullptr, P + L->pl.o, s.d, s.HD, s.HD, 1, 0, 0, hs);
+    e = llk::launch_pack(s.dt, w->v_proj, w->input_layernorm, P + L->pl.qkv, s.KD, s.d, s.d, s.NQKV_pad, 1, s.HD + s.KD, 0, hs);
+  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->o_proj, nullptr, P + L->pl.o, s.d, s.HD, s.HD, s.d_rows, 1, 0, 0, hs);
   // gate/up interleaved row by row; gamma_2 scales the activation instead
   // (h * gamma_2 is rounded once, the weights stay exact)
-  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->gate_proj, nullptr, P + L->pl.gu, s.I, s.d, s.d, 2, 0, 0, hs);
-  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->up_proj, nullptr, P + L->pl.gu, s.I, s.d, s.d, 2, 1, 0, hs);
+  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->gate_proj, nullptr, P + L->pl.gu, s.I, s.d, s.d, 2 * s.I_pad, 2, 0, 0, hs);
+  if (e == hipSuccess) e = llk::launch_pack(s.dt, w->up_proj, nullptr, P + L->pl.gu, s.I, s.d, s.d, 2 * s.I_pad, 2, 1, 0, hs);
   if (e == hipSuccess)
     e = llk::launch_to_f32(s.dt, w->post_attention_layernorm, reinterpret_cast<float*>(P + L->pl.gamma2), s.d, hs);
   if (e == hipSuccess)
-    e = llk::launch_pack(s.dt, w->down_proj, nullptr, P + L->pl.down, s.d, s.I, s.I_pad, 1, 0, 0, hs);
+    e = llk::launch_pack(s.dt, w->down_proj, nullptr, P + L->pl.down, s.d, s.I, s.I_pad, s.d_rows, 1, 0, 0, hs);
   if (e != hipSuccess) return fail(e);
 
   // RoPE table, angle pos * theta^(-2i/D) evaluated in double, stored fp32
@@ -781,6 +781,7 @@ llama_status run_layer(llama_layer* L, const llk::CacheView& cv, const llk::Batc
   a.X = xt ? xt : x;
   a.M = M;
   a.N = s.NQKV_pad;
+  a.w_rows = s.NQKV_pad;
   a.K = s.d;
   a.ldx = s.d;
   a.epi = llk::Epi::QKV;
@@ -812,6 +813,7 @@ llama_status run_layer(llama_layer* L, const llk::CacheView& cv, const llk::Batc
   o.X = attn;
   o.M = M;
   o.N = s.d;
+  o.w_rows = s.d_rows;
   o.K = s.HD;
   o.ldx = s.HD;
   o.epi = llk::Epi::RESID_H;
@@ -832,6 +834,7 @@ llama_status run_layer(llama_layer* L, const llk::CacheView& cv, const llk::Batc
   g.X = hb;
   g.M = M;
   g.N = 2 * s.I_pad;
+  g.w_rows = 2 * s.I_pad;
   g.K = s.d;
   g.ldx = s.d;
   g.epi = llk::Epi::SWIGLU;
@@ -848,6 +851,7 @@ llama_status run_layer(llama_layer* L, const llk::CacheView& cv, const llk::Batc
   dn.X = sb;
   dn.M = M;
   dn.N = s.d;
+  dn.w_rows = s.d_rows;
   dn.K = s.I_pad;
   dn.ldx = s.I_pad;
   dn.epi = llk::Epi::RESID_OUT;

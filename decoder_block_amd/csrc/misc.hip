@@ -8,11 +8,12 @@ namespace {
 
 // dst row (r * row_mul + row_add), columns [0, cols): src[r][c] * gamma[c],
 // computed in fp32 and rounded once to the storage type.  bf16 weights are
-// stored in 256 x 32 tiles (tiled_off, ldd columns); fp32 weights row-major.
+// stored K block first over drows rows (wtiled_off); fp32 weights row-major
+// with ldd columns.
 template <typename T>
 __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, const T* __restrict__ gamma,
-                                                   T* __restrict__ dst, int rows, int cols, int ldd, int row_mul,
-                                                   int row_add, int head_pairs) {
+                                                   T* __restrict__ dst, int rows, int cols, int ldd, int drows,
+                                                   int row_mul, int row_add, int head_pairs) {
   const size_t total = (size_t)rows * cols;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
     int r = (int)(i / cols);
@@ -25,7 +26,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const T* __restrict__ src, co
     }
     const int dr = r * row_mul + row_add;
     if constexpr (sizeof(T) == 2)
-      dst[tiled_off(dr, c, ldd)] = from_f32<T>(v);
+      dst[wtiled_off(dr, c, drows)] = from_f32<T>(v);
     else
       dst[(size_t)dr * ldd + c] = from_f32<T>(v);
   }
@@ -85,17 +86,17 @@ int grid_for(size_t n) {
 }  // namespace
 
 hipError_t launch_pack(DType t, const void* src, const void* gamma, void* dst, int rows, int cols, int ldd,
-                       int row_mul, int row_add, int head_pairs, hipStream_t s) {
+                       int drows, int row_mul, int row_add, int head_pairs, hipStream_t s) {
   if (head_pairs < 0 || head_pairs % 2 != 0 || (head_pairs > 0 && rows % head_pairs != 0)) return hipErrorInvalidValue;
   const int grid = grid_for((size_t)rows * cols);
   if (t == DType::BF16)
     pack_kernel<bf16><<<grid, 256, 0, s>>>(reinterpret_cast<const bf16*>(src), reinterpret_cast<const bf16*>(gamma),
-                                           reinterpret_cast<bf16*>(dst), rows, cols, ldd, row_mul, row_add,
+                                           reinterpret_cast<bf16*>(dst), rows, cols, ldd, drows, row_mul, row_add,
                                            head_pairs);
   else
     pack_kernel<float><<<grid, 256, 0, s>>>(reinterpret_cast<const float*>(src),
                                             reinterpret_cast<const float*>(gamma), reinterpret_cast<float*>(dst),
-                                            rows, cols, ldd, row_mul, row_add, head_pairs);
+                                            rows, cols, ldd, drows, row_mul, row_add, head_pairs);
   return hipGetLastError();
 }
 

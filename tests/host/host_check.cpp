@@ -25,7 +25,7 @@ static int g_fail = 0;
 static std::vector<std::string> g_log;
 static int g_events = 0;
 static int g_uploads = 0;
-struct PackCall { int rows, cols, ldd, row_mul, row_add, head_pairs; bool gamma; };
+struct PackCall { int rows, cols, ldd, drows, row_mul, row_add, head_pairs; bool gamma; };
 static std::vector<PackCall> g_packs;
 static int g_attn_units = -1;  // work units of the last decode-attention launch
 static std::vector<const void*> g_ins;   // x of each first-norm / final-norm launch
@@ -101,9 +101,9 @@ hipError_t event_elapsed_ms(float* ms, void*, void*) {
   *ms = 0.5f;
   return hipSuccess;
 }
-hipError_t launch_pack(DType, const void*, const void* gamma, void*, int rows, int cols, int ldd, int row_mul,
-                       int row_add, int head_pairs, hipStream_t) {
-  g_packs.push_back({rows, cols, ldd, row_mul, row_add, head_pairs, gamma != nullptr});
+hipError_t launch_pack(DType, const void*, const void* gamma, void*, int rows, int cols, int ldd, int drows,
+                       int row_mul, int row_add, int head_pairs, hipStream_t) {
+  g_packs.push_back({rows, cols, ldd, drows, row_mul, row_add, head_pairs, gamma != nullptr});
   return hipSuccess;
 }
 hipError_t launch_to_f32(DType, const void*, float* dst, int n, hipStream_t) {
@@ -224,6 +224,10 @@ int main() {
     CHECK(g_packs[4].row_mul == 2 && g_packs[4].row_add == 0 && !g_packs[4].gamma);
     CHECK(g_packs[5].row_mul == 2 && g_packs[5].row_add == 1 && !g_packs[5].gamma);
     CHECK(g_packs[6].cols == 688 && g_packs[6].ldd == 768 && !g_packs[6].gamma);
+    // destination rows of each packed matrix: qkv 512, o 256, gate/up 2 x 768, down 256
+    CHECK(g_packs[0].drows == 512 && g_packs[1].drows == 512 && g_packs[2].drows == 512);
+    CHECK(g_packs[3].drows == 256 && g_packs[4].drows == 1536 && g_packs[5].drows == 1536);
+    CHECK(g_packs[6].drows == 256);
     for (const PackCall& pc : g_packs) CHECK(pc.head_pairs == 0);  // interleaved RoPE: rows in order
   }
   // half-split RoPE: the q and k rows of each head are reordered, nothing else
