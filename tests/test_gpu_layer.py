@@ -466,3 +466,35 @@ def test_single_token_prefill_and_wide_decode_batch():
     torch.cuda.synchronize()
     r, _ = oracle.decode_step(_cfg(wd), wo_d, synth.as_f64(xt), host)
     P.assert_close(P.to_np(o), r, "bf16", "decode B=160")
+
+
+@pytest.mark.parametrize("n_new", [100, 128])
+def test_few_token_gemm_path_with_two_token_blocks(n_new):
+    # 65..128 tokens take the weight-streaming GEMMs with two 64-token blocks
+    # (the second ragged at 100): a continuation prefill of that many tokens
+    # after 250 cached ones (so every row attends to at least 250 keys, where
+    # the bf16 limits hold) and a decode batch of 100 sequences, against the
+    # oracle
+    w = synth.scaled(W[3], batch=1, seq_len=250 + n_new)
+    ws, wo = P.weights_for(w)
+    layer = P.make_layer(w, ws)
+    x = synth.layer_input(w)
+    cache = P.make_cache(layer, w, w.seq_len, 1, block_order_seed=21)
+    _, sids = P.gpu_prefill(layer, cache, x[:, :250].contiguous())
+    got, _ = P.gpu_prefill(layer, cache, x[:, 250:].contiguous(), sids=sids)
+    rows = list(range(250, 250 + n_new))
+    ref, k_ref, v_ref = oracle.prefill(_cfg(w), wo, synth.as_f64(x), rows=rows)
+    P.assert_close(P.to_np(got), ref, "bf16", f"continuation prefill of {n_new}")
+    k, v = cache.read(sids[0], 0, w.seq_len)
+    P.assert_close(P.to_np(k), k_ref[0], "bf16", "cached K")
+    P.assert_close(P.to_np(v), v_ref[0], "bf16", "cached V")
+    if n_new != 100:
+        return
+    wd = synth.scaled(W[4], batch=100, ctx_lo=16, ctx_hi=700)
+    layer_d, cache_d, sids_d, host, wo_d = _decode_setup(wd, block_seed=22)
+    for step in range(2):
+        xt = synth.decode_input(wd, step)
+        o = layer_d.decode(cache_d, sids_d, xt.cuda())
+        torch.cuda.synchronize()
+        r, host = oracle.decode_step(_cfg(wd), wo_d, synth.as_f64(xt), host)
+        P.assert_close(P.to_np(o), r, "bf16", f"decode B=100 step {step}")
