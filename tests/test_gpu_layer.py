@@ -498,3 +498,23 @@ def test_few_token_gemm_path_with_two_token_blocks(n_new):
         torch.cuda.synchronize()
         r, host = oracle.decode_step(_cfg(wd), wo_d, synth.as_f64(xt), host)
         P.assert_close(P.to_np(o), r, "bf16", f"decode B=100 step {step}")
+
+
+def test_hidden_size_not_a_multiple_of_256():
+    # d = 17 x 128 = 2176: the o_proj and down weights keep padding rows
+    # (2304 stored rows for 2176 features), so their K blocks are 2304 rows
+    # apart while the GEMMs produce 2176 features (64-wide tiles)
+    w = synth.scaled(W[3], hidden_size=2176, intermediate_size=5888, num_attention_heads=17,
+                     num_key_value_heads=17, batch=1, seq_len=300)
+    got, ref, (layer, cache, sids, k_ref, v_ref) = _prefill_case(w, block_seed=31)
+    P.assert_close(got, ref, "bf16", "d=2176 prefill")
+    k, v = cache.read(sids[0], 0, w.seq_len)
+    P.assert_close(P.to_np(k), k_ref[0], "bf16", "d=2176 cached K")
+    wd = synth.scaled(W[4], hidden_size=2176, intermediate_size=5888, num_attention_heads=17,
+                      num_key_value_heads=17, batch=4)
+    layer_d, cache_d, sids_d, host, wo = _decode_setup(wd, lens=[5, 300, 1025, 2000], block_seed=32)
+    xt = synth.decode_input(wd, 0)
+    o = layer_d.decode(cache_d, sids_d, xt.cuda())
+    torch.cuda.synchronize()
+    r, _ = oracle.decode_step(_cfg(wd), wo, synth.as_f64(xt), host)
+    P.assert_close(P.to_np(o), r, "bf16", "d=2176 decode")
