@@ -668,17 +668,28 @@ llama_status llama_kv_cache_write(llama_kv_cache* c, int32_t seq_id, int32_t n_t
                                   const void* v_dev, void* stream) {
   if (!c || !k_dev || !v_dev || n_tokens <= 0) return LLAMA_ERR_INVALID_ARG;
   Uploader up;
-  const int start = (seq_id >= 0 && seq_id < c->max_seqs) ? c->seqs[seq_id].len : 0;
+  const bool known = seq_id >= 0 && seq_id < c->max_seqs;
+  const int start = known ? c->seqs[seq_id].len : 0;
+  const size_t nblk = known ? c->seqs[seq_id].blocks.size() : 0;
   llama_status st = reserve(c, 1, &seq_id, n_tokens, &up);
   if (st != LLAMA_OK) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  HIP_TRY(up.flush(hs));
+  hipError_t e = up.flush(hs);
   const size_t per_layer = (size_t)n_tokens * c->s.KD * c->s.es;  // bytes of one layer's [n, G, D]
-  for (int l = 0; l < c->n_layers; ++l)
-    HIP_TRY(llk::launch_kv_copy(c->s.dt, cache_view(c, l), seq_id, start, n_tokens,
-                                const_cast<char*>(reinterpret_cast<const char*>(k_dev)) + l * per_layer,
-                                const_cast<char*>(reinterpret_cast<const char*>(v_dev)) + l * per_layer, true, hs));
-  c->seqs[seq_id].len += n_tokens;
+  for (int l = 0; l < c->n_layers && e == hipSuccess; ++l)
+    e = llk::launch_kv_copy(c->s.dt, cache_view(c, l), seq_id, start, n_tokens,
+                            const_cast<char*>(reinterpret_cast<const char*>(k_dev)) + l * per_layer,
+                            const_cast<char*>(reinterpret_cast<const char*>(v_dev)) + l * per_layer, true, hs);
+  SeqState& sq = c->seqs[seq_id];
+  if (e != hipSuccess) {  // give the reserved blocks back, newest first: the cache is as before the call
+    while (sq.blocks.size() > nblk) {
+      c->free_blocks.push_back(sq.blocks.back());
+      sq.blocks.pop_back();
+    }
+    if (trace_on()) std::fprintf(stderr, "[llama_layer] kv_cache_write: %s\n", hipGetErrorString(e));
+    return LLAMA_ERR_HIP;
+  }
+  sq.len += n_tokens;
   return LLAMA_OK;
 }
 
@@ -702,7 +713,8 @@ llama_status llama_kv_cache_read(const llama_kv_cache* c, int32_t seq_id, int32_
 
 namespace {
 
-// Argument checks common to a layer call and a stack call.
+// Argument checks common to a layer call and a stack call (the workspace size
+// is checked by the caller, once the call's layout is known).
 llama_status check_call(const Shape& s, const llama_kv_cache* c, int32_t batch, int32_t seq_len,
                         const int32_t* seq_ids, const void* x, const void* out, int32_t out_dtype,
                         const void* workspace) {
@@ -716,30 +728,65 @@ llama_status check_call(const Shape& s, const llama_kv_cache* c, int32_t batch, 
   return LLAMA_OK;
 }
 
-// Host bookkeeping of one call, shared by every layer it runs: reserve the
-// sequences' new blocks, queue the block-table and batch-descriptor stores
-// (all but the last batch of them launched here; the last rides on the first
-// kernel), and advance the sequence lengths.
-llama_status begin_call(llama_kv_cache* c, int32_t batch, int32_t seq_len, const int32_t* seq_ids, int32_t* desc,
-                        hipStream_t hs, const llk::Upload** last_upload, Uploader* up, int* attn_units) {
-  std::vector<int32_t> start(batch);
-  for (int b = 0; b < batch; ++b)
-    start[b] = (seq_ids[b] >= 0 && seq_ids[b] < c->max_seqs) ? c->seqs[seq_ids[b]].len : 0;
-  llama_status st = reserve(c, batch, seq_ids, seq_len, up);
-  if (st != LLAMA_OK) return st;
-  // (sequence, key chunk) work units of the decode attention after this call
-  const int ck = llk::decode_split_keys();
-  *attn_units = 0;
-  for (int b = 0; b < batch; ++b) *attn_units += (start[b] + seq_len + ck - 1) / ck;
-  for (int b = 0; b < batch; ++b) {
-    up->add(desc, 2 * b, seq_ids[b]);
-    up->add(desc, 2 * b + 1, start[b]);
+// Host bookkeeping of one forward call, shared by every layer it runs.
+// begin() reserves the sequences' new blocks and queues the block-table and
+// batch-descriptor stores (all but the last batch of them launched here; the
+// last rides on the first kernel).  commit() advances the sequence lengths
+// once every kernel of the call has been enqueued; abort() instead returns
+// the blocks reserved by begin() to the pool, in the order they were taken,
+// so a failed call leaves the cache as it found it.
+struct CallBook {
+  llama_kv_cache* c = nullptr;
+  int batch = 0, seq_len = 0;
+  const int32_t* seq_ids = nullptr;
+  std::vector<int> nblocks;  // blocks of each sequence before the call
+  bool reserved = false;
+
+  llama_status begin(llama_kv_cache* cache, int32_t b_, int32_t s_, const int32_t* ids, int32_t* desc, hipStream_t hs,
+                     const llk::Upload** last_upload, Uploader* up, int* attn_units) {
+    c = cache;
+    batch = b_;
+    seq_len = s_;
+    seq_ids = ids;
+    std::vector<int32_t> start(batch);
+    nblocks.assign(batch, 0);
+    for (int b = 0; b < batch; ++b) {
+      const bool known = seq_ids[b] >= 0 && seq_ids[b] < c->max_seqs;
+      start[b] = known ? c->seqs[seq_ids[b]].len : 0;
+      nblocks[b] = known ? (int)c->seqs[seq_ids[b]].blocks.size() : 0;
+    }
+    llama_status st = reserve(c, batch, seq_ids, seq_len, up);
+    if (st != LLAMA_OK) return st;  // reserve changes nothing when it fails
+    reserved = true;
+    // (sequence, key chunk) work units of the decode attention after this call
+    const int ck = llk::decode_split_keys();
+    *attn_units = 0;
+    for (int b = 0; b < batch; ++b) *attn_units += (start[b] + seq_len + ck - 1) / ck;
+    for (int b = 0; b < batch; ++b) {
+      up->add(desc, 2 * b, seq_ids[b]);
+      up->add(desc, 2 * b + 1, start[b]);
+    }
+    HIP_TRY(up->flush_all_but_last(hs, last_upload));
+    return LLAMA_OK;
   }
-  // lengths are committed now: every later failure is a device failure
-  for (int b = 0; b < batch; ++b) c->seqs[seq_ids[b]].len += seq_len;
-  HIP_TRY(up->flush_all_but_last(hs, last_upload));
-  return LLAMA_OK;
-}
+  void commit() {
+    for (int b = 0; b < batch; ++b) c->seqs[seq_ids[b]].len += seq_len;
+    reserved = false;
+  }
+  void abort() {
+    if (!reserved) return;
+    // reserve() took blocks from the back of the free list, sequence by
+    // sequence; putting them back in reverse restores the list exactly
+    for (int b = batch - 1; b >= 0; --b) {
+      SeqState& st = c->seqs[seq_ids[b]];
+      while ((int)st.blocks.size() > nblocks[b]) {
+        c->free_blocks.push_back(st.blocks.back());
+        st.blocks.pop_back();
+      }
+    }
+    reserved = false;
+  }
+};
 
 // The kernels of one layer over the tokens of a call (begin_call done):
 // x [M][d] in the layer dtype -> out [M][d] in out_t; K/V of the new tokens
@@ -864,7 +911,8 @@ llama_status run_layer(llama_layer* L, const llk::CacheView& cv, const llk::Batc
 }
 
 llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, int32_t seq_len, const int32_t* seq_ids,
-                     const void* x, void* out, int32_t out_dtype, void* workspace, void* stream, bool decode) {
+                     const void* x, void* out, int32_t out_dtype, void* workspace, size_t ws_bytes, void* stream,
+                     bool decode) {
   if (!L) return LLAMA_ERR_INVALID_ARG;
   llama_status st = check_call(L->s, c, batch, seq_len, seq_ids, x, out, out_dtype, workspace);
   if (st != LLAMA_OK) return st;
@@ -872,17 +920,23 @@ llama_status forward(llama_layer* L, llama_kv_cache* c, int32_t batch, int32_t s
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const int M = batch * seq_len;
   const WsLayout wl = ws_layout(L->s, (size_t)M, (size_t)batch);
+  if (ws_bytes < wl.total) return LLAMA_ERR_INVALID_ARG;
   char* W = reinterpret_cast<char*>(workspace);
   int32_t* desc = reinterpret_cast<int32_t*>(W + wl.desc);
   if (poison_on()) HIP_TRY(llk::launch_fill(W, wl.total, 0xFF, hs));  // before the uploads into it
   Uploader up;
   const llk::Upload* last_upload = nullptr;
   int units = 0;
-  st = begin_call(c, batch, seq_len, seq_ids, desc, hs, &last_upload, &up, &units);
-  if (st != LLAMA_OK) return st;
-  const llk::BatchView bv{desc, batch, seq_len};
-  return run_layer(L, cache_view(c), bv, M, x, out, out_dtype == LLAMA_DTYPE_F32 ? DType::F32 : DType::BF16, W, wl,
+  CallBook book;
+  st = book.begin(c, batch, seq_len, seq_ids, desc, hs, &last_upload, &up, &units);
+  if (st == LLAMA_OK) {
+    const llk::BatchView bv{desc, batch, seq_len};
+    st = run_layer(L, cache_view(c), bv, M, x, out, out_dtype == LLAMA_DTYPE_F32 ? DType::F32 : DType::BF16, W, wl,
                    last_upload, hs, decode, units);
+  }
+  if (st == LLAMA_OK) book.commit();
+  else book.abort();
+  return st;
 }
 
 }  // namespace
@@ -928,7 +982,7 @@ StackWs stack_ws(const Shape& s, size_t T, size_t B) {
 
 llama_status stack_forward(llama_stack* S, llama_kv_cache* c, int32_t batch, int32_t seq_len,
                            const int32_t* seq_ids, const void* x, void* out, int32_t out_dtype, void* workspace,
-                           void* stream, bool decode) {
+                           size_t ws_bytes, void* stream, bool decode) {
   if (!S) return LLAMA_ERR_INVALID_ARG;
   llama_layer* L0 = S->layers[0];
   llama_status st = check_call(L0->s, c, batch, seq_len, seq_ids, x, out, out_dtype, workspace);
@@ -938,31 +992,36 @@ llama_status stack_forward(llama_stack* S, llama_kv_cache* c, int32_t batch, int
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   const int M = batch * seq_len;
   const StackWs sw = stack_ws(L0->s, (size_t)M, (size_t)batch);
+  if (ws_bytes < sw.total) return LLAMA_ERR_INVALID_ARG;
   char* W = reinterpret_cast<char*>(workspace);
   int32_t* desc = reinterpret_cast<int32_t*>(W + sw.layer.desc);
   if (poison_on()) HIP_TRY(llk::launch_fill(W, sw.total, 0xFF, hs));  // before the uploads into it
   Uploader up;
   const llk::Upload* last_upload = nullptr;
   int units = 0;
-  st = begin_call(c, batch, seq_len, seq_ids, desc, hs, &last_upload, &up, &units);
-  if (st != LLAMA_OK) return st;
+  CallBook book;
+  st = book.begin(c, batch, seq_len, seq_ids, desc, hs, &last_upload, &up, &units);
   const llk::BatchView bv{desc, batch, seq_len};
   // x_{l+1} = layer_l(x_l), held in the layer dtype between layers
   const void* cur = x;
-  for (int l = 0; l < nl; ++l) {
+  for (int l = 0; l < nl && st == LLAMA_OK; ++l) {
     void* nxt = W + sw.act[l & 1];
     st = run_layer(S->layers[l], cache_view(c, l), bv, M, cur, nxt, L0->s.dt, W, sw.layer,
                    l == 0 ? last_upload : nullptr, hs, decode, units);
-    if (st != LLAMA_OK) return st;
     cur = nxt;
   }
   // y = RMSNorm_final(x_L), timed with the last layer's kernels
-  llama_layer* Ll = S->layers[nl - 1];
-  const DType out_t = out_dtype == LLAMA_DTYPE_F32 ? DType::F32 : DType::BF16;
-  HIP_TRY(timed(Ll, K_FINAL_NORM, hs, [&] {
-    return llk::launch_rms_norm_out(L0->s.dt, cur, S->final_norm, out, out_t, M, L0->s.d, L0->cfg.rms_norm_eps, hs);
-  }));
-  return LLAMA_OK;
+  if (st == LLAMA_OK) {
+    llama_layer* Ll = S->layers[nl - 1];
+    const DType out_t = out_dtype == LLAMA_DTYPE_F32 ? DType::F32 : DType::BF16;
+    const hipError_t e = timed(Ll, K_FINAL_NORM, hs, [&] {
+      return llk::launch_rms_norm_out(L0->s.dt, cur, S->final_norm, out, out_t, M, L0->s.d, L0->cfg.rms_norm_eps, hs);
+    });
+    if (e != hipSuccess) st = LLAMA_ERR_HIP;
+  }
+  if (st == LLAMA_OK) book.commit();
+  else book.abort();
+  return st;
 }
 
 }  // namespace
@@ -1000,24 +1059,27 @@ llama_status llama_stack_destroy(llama_stack* S) {
 
 llama_status llama_stack_prefill(llama_stack* stack, llama_kv_cache* cache, int32_t batch, int32_t seq_len,
                                  const int32_t* seq_ids, const void* x, void* out, int32_t out_dtype,
-                                 void* workspace, void* stream) {
-  return stack_forward(stack, cache, batch, seq_len, seq_ids, x, out, out_dtype, workspace, stream, false);
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return stack_forward(stack, cache, batch, seq_len, seq_ids, x, out, out_dtype, workspace, workspace_bytes, stream,
+                       false);
 }
 
 llama_status llama_stack_decode(llama_stack* stack, llama_kv_cache* cache, int32_t batch, const int32_t* seq_ids,
-                                const void* x, void* out, int32_t out_dtype, void* workspace, void* stream) {
-  return stack_forward(stack, cache, batch, 1, seq_ids, x, out, out_dtype, workspace, stream, true);
+                                const void* x, void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return stack_forward(stack, cache, batch, 1, seq_ids, x, out, out_dtype, workspace, workspace_bytes, stream, true);
 }
 
 llama_status llama_layer_prefill(llama_layer* layer, llama_kv_cache* cache, int32_t batch, int32_t seq_len,
                                  const int32_t* seq_ids, const void* x, void* out, int32_t out_dtype,
-                                 void* workspace, void* stream) {
-  return forward(layer, cache, batch, seq_len, seq_ids, x, out, out_dtype, workspace, stream, false);
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  return forward(layer, cache, batch, seq_len, seq_ids, x, out, out_dtype, workspace, workspace_bytes, stream, false);
 }
 
 llama_status llama_layer_decode(llama_layer* layer, llama_kv_cache* cache, int32_t batch, const int32_t* seq_ids,
-                                const void* x, void* out, int32_t out_dtype, void* workspace, void* stream) {
-  return forward(layer, cache, batch, 1, seq_ids, x, out, out_dtype, workspace, stream, true);
+                                const void* x, void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  return forward(layer, cache, batch, 1, seq_ids, x, out, out_dtype, workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -86,8 +86,8 @@ def lib() -> ctypes.CDLL:
         "llama_kv_cache_free_blocks": (ctypes.c_int, [P, ctypes.POINTER(I32)]),
         "llama_kv_cache_write": (ctypes.c_int, [P, I32, I32, P, P, P]),
         "llama_kv_cache_read": (ctypes.c_int, [P, I32, I32, I32, P, P, P]),
-        "llama_layer_prefill": (ctypes.c_int, [P, P, I32, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, P]),
-        "llama_layer_decode": (ctypes.c_int, [P, P, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, P]),
+        "llama_layer_prefill": (ctypes.c_int, [P, P, I32, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, SZ, P]),
+        "llama_layer_decode": (ctypes.c_int, [P, P, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, SZ, P]),
         "llama_layer_profile_enable": (ctypes.c_int, [P, I32]),
         "llama_layer_profile_read": (ctypes.c_int, [P, ctypes.POINTER(LlamaKernelTime), I32, ctypes.POINTER(I32), I32]),
         "llama_kv_cache_bytes_layers": (ctypes.c_int, [cfgp, I32, I32, I32, I32, ctypes.POINTER(SZ)]),
@@ -97,8 +97,8 @@ def lib() -> ctypes.CDLL:
         "llama_stack_create": (ctypes.c_int, [ctypes.POINTER(P), I32, P, ctypes.POINTER(P)]),
         "llama_stack_workspace_bytes": (ctypes.c_int, [P, I32, I32, ctypes.POINTER(SZ)]),
         "llama_stack_destroy": (ctypes.c_int, [P]),
-        "llama_stack_prefill": (ctypes.c_int, [P, P, I32, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, P]),
-        "llama_stack_decode": (ctypes.c_int, [P, P, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, P]),
+        "llama_stack_prefill": (ctypes.c_int, [P, P, I32, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, SZ, P]),
+        "llama_stack_decode": (ctypes.c_int, [P, P, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -229,15 +229,27 @@ def llama_stack_destroy(stack):
     _check(lib().llama_stack_destroy(stack), "llama_stack_destroy")
 
 
+def _nbytes(t, nbytes):
+    """Size of a workspace argument: the tensor's bytes unless given explicitly."""
+    if nbytes is not None:
+        return int(nbytes)
+    if isinstance(t, torch.Tensor):
+        return t.numel() * t.element_size()
+    raise ValueError("workspace given as an address needs workspace_bytes")
+
+
 def llama_stack_prefill(stack, cache, batch: int, seq_len: int, seq_ids, x, out, out_dtype: int,
-                        workspace, stream=None):
+                        workspace, stream=None, workspace_bytes=None):
     _check(lib().llama_stack_prefill(stack, cache, batch, seq_len, _i32_array(seq_ids), _ptr(x), _ptr(out),
-                                     out_dtype, _ptr(workspace), _stream(stream)), "llama_stack_prefill")
+                                     out_dtype, _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                     _stream(stream)), "llama_stack_prefill")
 
 
-def llama_stack_decode(stack, cache, batch: int, seq_ids, x, out, out_dtype: int, workspace, stream=None):
+def llama_stack_decode(stack, cache, batch: int, seq_ids, x, out, out_dtype: int, workspace, stream=None,
+                       workspace_bytes=None):
     _check(lib().llama_stack_decode(stack, cache, batch, _i32_array(seq_ids), _ptr(x), _ptr(out), out_dtype,
-                                    _ptr(workspace), _stream(stream)), "llama_stack_decode")
+                                    _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)),
+           "llama_stack_decode")
 
 
 def llama_kv_cache_destroy(cache):
@@ -277,14 +289,17 @@ def llama_kv_cache_read(cache, seq_id: int, start: int, n: int, k_dev, v_dev, st
 
 
 def llama_layer_prefill(layer, cache, batch: int, seq_len: int, seq_ids, x, out, out_dtype: int,
-                        workspace, stream=None):
+                        workspace, stream=None, workspace_bytes=None):
     _check(lib().llama_layer_prefill(layer, cache, batch, seq_len, _i32_array(seq_ids), _ptr(x), _ptr(out),
-                                     out_dtype, _ptr(workspace), _stream(stream)), "llama_layer_prefill")
+                                     out_dtype, _ptr(workspace), _nbytes(workspace, workspace_bytes),
+                                     _stream(stream)), "llama_layer_prefill")
 
 
-def llama_layer_decode(layer, cache, batch: int, seq_ids, x, out, out_dtype: int, workspace, stream=None):
+def llama_layer_decode(layer, cache, batch: int, seq_ids, x, out, out_dtype: int, workspace, stream=None,
+                       workspace_bytes=None):
     _check(lib().llama_layer_decode(layer, cache, batch, _i32_array(seq_ids), _ptr(x), _ptr(out), out_dtype,
-                                    _ptr(workspace), _stream(stream)), "llama_layer_decode")
+                                    _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)),
+           "llama_layer_decode")
 
 
 def llama_layer_profile_enable(layer, enable: bool):

@@ -187,7 +187,8 @@ llama_status llama_kv_cache_free_blocks(const llama_kv_cache* cache, int32_t* n)
 /* Append n_tokens already-rotated keys and values ([n, G, D] each, device,
  * cfg.dtype; [n_layers, n, G, D] for a multi-layer cache) to a sequence
  * (positions len .. len+n-1).  Used to restore a saved cache or to pre-fill
- * one. */
+ * one.  The length advances after the copies are enqueued; if a launch fails
+ * (LLAMA_ERR_HIP) the blocks reserved for the call go back to the pool. */
 llama_status llama_kv_cache_write(llama_kv_cache* cache, int32_t seq_id, int32_t n_tokens,
                                   const void* k_dev, const void* v_dev, void* stream);
 
@@ -204,18 +205,30 @@ llama_status llama_kv_cache_read(const llama_kv_cache* cache, int32_t seq_id, in
  * seq_ids: host array of `batch` distinct open sequences.  Sequence b's new
  * tokens take positions len_b .. len_b+seq_len-1 and see every cached key
  * at or before their position; their K/V are appended to the cache.
- * workspace: device, llama_layer_workspace_bytes(batch*seq_len, batch). */
+ * workspace: device scratch of workspace_bytes bytes (caller-owned, 256-byte
+ * aligned, contents need not be initialised and are not kept between calls);
+ * a workspace_bytes below llama_layer_workspace_bytes(batch*seq_len, batch)
+ * is rejected with LLAMA_ERR_INVALID_ARG before any device work.
+ * Cache bookkeeping: the sequence lengths advance only once every kernel of
+ * the call has been enqueued.  If a launch fails (LLAMA_ERR_HIP) the lengths
+ * and the block allocation are restored to their state before the call (the
+ * K/V the call already wrote sit past the restored lengths and are
+ * overwritten by the next call). */
 llama_status llama_layer_prefill(llama_layer* layer, llama_kv_cache* cache, int32_t batch,
                                  int32_t seq_len, const int32_t* seq_ids, const void* x,
-                                 void* out, int32_t out_dtype, void* workspace, void* stream);
+                                 void* out, int32_t out_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* One decode step: token b sits at position len_b of sequence seq_ids[b],
  * is appended to the cache and attends to all len_b + 1 keys.
  * x: [batch, d]; out: [batch, d] in out_dtype.
- * workspace: device, llama_layer_workspace_bytes(batch, batch). */
+ * workspace / workspace_bytes: as for prefill, with at least
+ * llama_layer_workspace_bytes(batch, batch) bytes.  Bookkeeping and failure
+ * behaviour as for prefill. */
 llama_status llama_layer_decode(llama_layer* layer, llama_kv_cache* cache, int32_t batch,
                                 const int32_t* seq_ids, const void* x, void* out,
-                                int32_t out_dtype, void* workspace, void* stream);
+                                int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* ---- stack of layers + final RMSNorm ---------------------------------- */
 
@@ -244,16 +257,20 @@ llama_status llama_stack_destroy(llama_stack* stack);
 /* Prefill / decode through every layer and the final norm, with the
  * arguments and semantics of llama_layer_prefill / llama_layer_decode; cache
  * must have been created with n_layers equal to the stack's (else
- * LLAMA_ERR_SHAPE).  Layer l reads and appends the K/V of its own pools; the
- * sequence lengths advance once per call.  out holds y.  Per-kernel timing
- * is recorded by each layer's handle; the final norm ("rms_final_norm") is
- * counted with the last layer. */
+ * LLAMA_ERR_SHAPE); workspace_bytes must be at least
+ * llama_stack_workspace_bytes for the call (else LLAMA_ERR_INVALID_ARG).
+ * Layer l reads and appends the K/V of its own pools; the sequence lengths
+ * advance once per call, after the last launch (restored if a launch fails).
+ * out holds y.  Per-kernel timing is recorded by each layer's handle; the
+ * final norm ("rms_final_norm") is counted with the last layer. */
 llama_status llama_stack_prefill(llama_stack* stack, llama_kv_cache* cache, int32_t batch,
                                  int32_t seq_len, const int32_t* seq_ids, const void* x,
-                                 void* out, int32_t out_dtype, void* workspace, void* stream);
+                                 void* out, int32_t out_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 llama_status llama_stack_decode(llama_stack* stack, llama_kv_cache* cache, int32_t batch,
                                 const int32_t* seq_ids, const void* x, void* out,
-                                int32_t out_dtype, void* workspace, void* stream);
+                                int32_t out_dtype, void* workspace, size_t workspace_bytes,
+                                void* stream);
 
 /* ---- measurement ------------------------------------------------------ */
 

@@ -32,6 +32,9 @@ static std::vector<const void*> g_ins;   // x of each first-norm / final-norm la
 static std::vector<void*> g_outs;        // out of each down-projection launch
 struct FinalCall { const void* gamma; void* y; };
 static FinalCall g_final = {nullptr, nullptr};
+// name of a stubbed launch that fails (empty: none), to test the rollback of a failed call
+static std::string g_fail_launch;
+static bool fails(const char* what) { return g_fail_launch == what; }
 
 namespace llk {
 int gemm_tile_n(GemmTile t) { return t == GemmTile::LARGE ? 256 : 64; }
@@ -43,6 +46,7 @@ size_t skinny_partial_bytes(int M, int N, int K) {
 hipError_t launch_gemm(DType, GemmTile t, const GemmArgs& a, hipStream_t) {
   const char* tag = t == GemmTile::LARGE ? "L" : (t == GemmTile::SKINNY ? "K" : "S");
   g_log.push_back("gemm" + std::to_string((int)a.epi) + tag);
+  if (fails(g_log.back().c_str())) return hipErrorLaunchFailure;
   if (a.epi == Epi::RESID_OUT) g_outs.push_back(a.out);
   if (t == GemmTile::SKINNY && a.split_ws_bytes < skinny_partial_bytes(a.M, a.N, a.K)) g_log.push_back("gemm-ws-short");
   return hipSuccess;
@@ -69,18 +73,18 @@ hipError_t launch_rms_norm_out(DType, const void* x, const void* gamma, void* y,
   g_log.push_back("rms_final");
   g_ins.push_back(x);
   g_final = {gamma, y};
-  return hipSuccess;
+  return fails("rms_final") ? hipErrorLaunchFailure : hipSuccess;
 }
 hipError_t launch_attn_prefill(DType, const void*, void*, int, const CacheView&, const BatchView&, hipStream_t) {
   g_log.push_back("attn_prefill");
-  return hipSuccess;
+  return fails("attn_prefill") ? hipErrorLaunchFailure : hipSuccess;
 }
 int decode_split_keys() { return 1024; }
 hipError_t launch_attn_decode(DType, const void*, float*, int, int, const CacheView&, const BatchView&, int units,
                               hipStream_t) {
   g_attn_units = units;
   g_log.push_back("attn_decode");
-  return hipSuccess;
+  return fails("attn_decode") ? hipErrorLaunchFailure : hipSuccess;
 }
 hipError_t launch_attn_decode_combine(DType, const float*, void*, int, int, int, const BatchView&, hipStream_t) {
   g_log.push_back("attn_combine");
@@ -131,6 +135,7 @@ hipError_t copy_to_device(void* dst, const void* src, size_t bytes, hipStream_t)
 hipError_t stream_sync(hipStream_t) { return hipSuccess; }
 hipError_t launch_kv_copy(DType t, const CacheView& c, int seq, int start, int n, void* k, void* v, bool to_cache,
                           hipStream_t) {
+  if (fails("kv_copy")) return hipErrorLaunchFailure;
   const size_t es = t == DType::F32 ? 4 : 2;
   char* kp = (char*)c.k_pool;
   char* vp = (char*)c.v_pool;
@@ -284,13 +289,14 @@ int main() {
   CHECK(llama_kv_cache_free_seq(C, s2) == LLAMA_ERR_BAD_SEQ);
 
   // prefill 2 x 20 tokens: 2 blocks each, handed out in `order`
-  void* ws = aligned_buf(1 << 22);
+  const size_t kWsBytes = 1 << 22;
+  void* ws = aligned_buf(kWsBytes);
   void* x = aligned_buf(2 * 20 * 256 * 4);
   void* out = aligned_buf(2 * 20 * 256 * 4);
   int32_t ids[2] = {s0, s1};
   g_log.clear();
-  CHECK(llama_layer_prefill(L, C, 2, 20, ids, x, out, LLAMA_DTYPE_BF16, ws, nullptr) == LLAMA_ERR_DTYPE);
-  CHECK(llama_layer_prefill(L, C, 2, 20, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+  CHECK(llama_layer_prefill(L, C, 2, 20, ids, x, out, LLAMA_DTYPE_BF16, ws, kWsBytes, nullptr) == LLAMA_ERR_DTYPE);
+  CHECK(llama_layer_prefill(L, C, 2, 20, ids, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_OK);
   {
     const std::vector<std::string> want = {"rms1", "gemm0S", "attn_prefill", "gemm1S", "rms2", "gemm2S", "gemm3S"};
     CHECK(g_log == want);
@@ -312,23 +318,51 @@ int main() {
 
   // errors leave the state unchanged
   int32_t dup[2] = {s0, s0};
-  CHECK(llama_layer_prefill(L, C, 2, 4, dup, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_ERR_BAD_SEQ);
+  CHECK(llama_layer_prefill(L, C, 2, 4, dup, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_ERR_BAD_SEQ);
   int32_t unk[1] = {2};
-  CHECK(llama_layer_decode(L, C, 1, unk, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_ERR_BAD_SEQ);
-  CHECK(llama_layer_prefill(L, C, 1, 61, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_ERR_POSITION);
-  CHECK(llama_layer_prefill(L, C, 2, 60, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_ERR_CACHE_FULL);
+  CHECK(llama_layer_decode(L, C, 1, unk, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_ERR_BAD_SEQ);
+  CHECK(llama_layer_prefill(L, C, 1, 61, ids, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_ERR_POSITION);
+  CHECK(llama_layer_prefill(L, C, 2, 60, ids, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_ERR_CACHE_FULL);
   CHECK(llama_kv_cache_seq_len(C, s0, &n) == LLAMA_OK && n == 20);
   CHECK(llama_kv_cache_free_blocks(C, &n) == LLAMA_OK && n == NB - 4);
-  CHECK(llama_layer_prefill(L, C, 1, 4, ids, (char*)x + 4, out, LLAMA_DTYPE_F32, ws, nullptr) ==
+  CHECK(llama_layer_prefill(L, C, 1, 4, ids, (char*)x + 4, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) ==
         LLAMA_ERR_INVALID_ARG);
+
+  // a workspace smaller than the call needs is refused before any device work
+  {
+    size_t need = 0;
+    CHECK(llama_layer_workspace_bytes(L, 2 * 4, 2, &need) == LLAMA_OK && need <= kWsBytes);
+    g_log.clear();
+    CHECK(llama_layer_prefill(L, C, 2, 4, ids, x, out, LLAMA_DTYPE_F32, ws, need - 1, nullptr) ==
+          LLAMA_ERR_INVALID_ARG);
+    CHECK(llama_layer_decode(L, C, 2, ids, x, out, LLAMA_DTYPE_F32, ws, 0, nullptr) == LLAMA_ERR_INVALID_ARG);
+    CHECK(g_log.empty());
+    CHECK(llama_kv_cache_seq_len(C, s0, &n) == LLAMA_OK && n == 20);
+    CHECK(llama_kv_cache_free_blocks(C, &n) == LLAMA_OK && n == NB - 4);
+  }
+  // a launch that fails part-way leaves lengths, blocks and the free list as they were
+  {
+    const std::vector<int32_t> tab_before(tab, tab + 3 * maxb);
+    for (const char* k : {"attn_prefill", "gemm3S"}) {
+      g_fail_launch = k;
+      CHECK(llama_layer_prefill(L, C, 2, 13, ids, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_ERR_HIP);
+      g_fail_launch.clear();
+      CHECK(llama_kv_cache_seq_len(C, s0, &n) == LLAMA_OK && n == 20);
+      CHECK(llama_kv_cache_seq_len(C, s1, &n) == LLAMA_OK && n == 20);
+      CHECK(llama_kv_cache_free_blocks(C, &n) == LLAMA_OK && n == NB - 4);
+    }
+    CHECK(tab_before[0] == tab[0] && tab_before[1] == tab[1] && tab_before[maxb + 1] == tab[maxb + 1]);
+    // the decode below takes order[4] for seq 0's third block: the free list
+    // came back in its original order
+  }
 
   // decode: 12 steps on seq 0 (20 -> 32 crosses into a third block only at 32)
   g_log.clear();
   for (int t = 0; t < 12; ++t)
-    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_OK);
   CHECK(llama_kv_cache_seq_len(C, s0, &n) == LLAMA_OK && n == 32);
   CHECK(llama_kv_cache_free_blocks(C, &n) == LLAMA_OK && n == NB - 4);
-  CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+  CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_OK);
   CHECK(llama_kv_cache_free_blocks(C, &n) == LLAMA_OK && n == NB - 5);
   CHECK(tab[0 * maxb + 2] == 0);  // order[4]
   CHECK(desc[0] == s0 && desc[1] == 32);
@@ -339,12 +373,12 @@ int main() {
   {
     setenv("LLAMA_LAYER_POISON", "1", 1);
     g_log.clear();
-    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_OK);
     CHECK(!g_log.empty() && g_log[0] == "fill" && g_log.size() == 9);
     CHECK(desc[0] == s0 && desc[1] == 33);  // descriptors written after the fill
     unsetenv("LLAMA_LAYER_POISON");
     g_log.clear();
-    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_OK);
     CHECK(g_log.size() == 8 && g_log[0] == "rms1");
     CHECK(desc[1] == 34);
   }
@@ -352,8 +386,8 @@ int main() {
   // per-kernel timing: two events per launch, totals per kernel family
   {
     CHECK(llama_layer_profile_enable(L, 1) == LLAMA_OK);
-    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
-    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, nullptr) == LLAMA_OK);
+    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_OK);
+    CHECK(llama_layer_decode(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, ws, kWsBytes, nullptr) == LLAMA_OK);
     llama_kernel_time kt[16];
     int32_t nk = 0;
     CHECK(llama_layer_profile_read(L, kt, 16, &nk, 1) == LLAMA_OK && nk == 8);
@@ -379,6 +413,13 @@ int main() {
       k[i] = (float)i;
       v[i] = -(float)i;
     }
+    int32_t fb0 = 0, fb1 = 0;
+    CHECK(llama_kv_cache_free_blocks(C, &fb0) == LLAMA_OK);
+    g_fail_launch = "kv_copy";
+    CHECK(llama_kv_cache_write(C, s, 30, k.data(), v.data(), nullptr) == LLAMA_ERR_HIP);
+    g_fail_launch.clear();
+    CHECK(llama_kv_cache_free_blocks(C, &fb1) == LLAMA_OK && fb1 == fb0);
+    CHECK(llama_kv_cache_seq_len(C, s, &n) == LLAMA_OK && n == 0);
     CHECK(llama_kv_cache_write(C, s, 30, k.data(), v.data(), nullptr) == LLAMA_OK);
     CHECK(llama_kv_cache_write(C, s, 7, k.data() + 30 * G * D, v.data() + 30 * G * D, nullptr) == LLAMA_OK);
     CHECK(llama_kv_cache_read(C, s, 0, ntok, k2.data(), v2.data(), nullptr) == LLAMA_OK);
@@ -419,18 +460,18 @@ int main() {
     void* ob = aligned_buf(2 * 300 * 256 * 4);
     int32_t ids2[2] = {sa, sb};
     g_log.clear();
-    CHECK(llama_layer_prefill(Lb, Cb, 2, 50, ids2, xb, ob, LLAMA_DTYPE_F32, wsb2, nullptr) == LLAMA_OK);
+    CHECK(llama_layer_prefill(Lb, Cb, 2, 50, ids2, xb, ob, LLAMA_DTYPE_F32, wsb2, w1000, nullptr) == LLAMA_OK);
     {
       const std::vector<std::string> want = {"rms1", "gemm0K", "attn_prefill", "gemm1K", "rms2", "gemm2K", "gemm3K"};
       CHECK(g_log == want);
     }
     g_log.clear();
     const int uploads_before = g_uploads;
-    CHECK(llama_layer_decode(Lb, Cb, 2, ids2, xb, ob, LLAMA_DTYPE_BF16, wsb2, nullptr) == LLAMA_OK);
+    CHECK(llama_layer_decode(Lb, Cb, 2, ids2, xb, ob, LLAMA_DTYPE_BF16, wsb2, w1000, nullptr) == LLAMA_OK);
     CHECK(g_uploads == uploads_before);  // block table + descriptors ride on the first norm launch
     CHECK(g_log.size() == 8 && g_log[1] == "gemm0K" && g_log[7] == "gemm3K");
     g_log.clear();
-    CHECK(llama_layer_prefill(Lb, Cb, 1, 300, ids2, xb, ob, LLAMA_DTYPE_F32, wsb2, nullptr) == LLAMA_OK);
+    CHECK(llama_layer_prefill(Lb, Cb, 1, 300, ids2, xb, ob, LLAMA_DTYPE_F32, wsb2, w1000, nullptr) == LLAMA_OK);
     {
       const std::vector<std::string> want = {"rms1", "gemm0L", "attn_prefill", "gemm1L", "rms2", "gemm2L", "gemm3L"};
       CHECK(g_log == want);
@@ -499,21 +540,21 @@ int main() {
     void* x3 = aligned_buf(40 * 256 * 4);
     void* y3 = aligned_buf(40 * 256 * 4);
     // a multi-layer cache is the stack's; a single-layer cache is the layer's
-    CHECK(llama_layer_prefill(Ls[0], C3, 2, 20, sids, x3, y3, LLAMA_DTYPE_F32, ws3, nullptr) == LLAMA_ERR_SHAPE);
+    CHECK(llama_layer_prefill(Ls[0], C3, 2, 20, sids, x3, y3, LLAMA_DTYPE_F32, ws3, wsz, nullptr) == LLAMA_ERR_SHAPE);
     llama_kv_cache* C1 = nullptr;
     void* pool1 = aligned_buf(b1);
     CHECK(llama_kv_cache_create(&cs, 6, 16, 2, nullptr, pool1, &C1) == LLAMA_OK);
     int32_t s1a = -1;
     CHECK(llama_kv_cache_add_seq(C1, &s1a) == LLAMA_OK);
-    CHECK(llama_stack_prefill(S, C1, 1, 20, &s1a, x3, y3, LLAMA_DTYPE_F32, ws3, nullptr) == LLAMA_ERR_SHAPE);
+    CHECK(llama_stack_prefill(S, C1, 1, 20, &s1a, x3, y3, LLAMA_DTYPE_F32, ws3, wsz, nullptr) == LLAMA_ERR_SHAPE);
     CHECK(llama_kv_cache_destroy(C1) == LLAMA_OK);
     std::free(pool1);
-    CHECK(llama_stack_prefill(S, C3, 2, 20, sids, x3, y3, LLAMA_DTYPE_BF16, ws3, nullptr) == LLAMA_ERR_DTYPE);
+    CHECK(llama_stack_prefill(S, C3, 2, 20, sids, x3, y3, LLAMA_DTYPE_BF16, ws3, wsz, nullptr) == LLAMA_ERR_DTYPE);
 
     g_log.clear();
     g_ins.clear();
     g_outs.clear();
-    CHECK(llama_stack_prefill(S, C3, 2, 20, sids, x3, y3, LLAMA_DTYPE_F32, ws3, nullptr) == LLAMA_OK);
+    CHECK(llama_stack_prefill(S, C3, 2, 20, sids, x3, y3, LLAMA_DTYPE_F32, ws3, wsz, nullptr) == LLAMA_OK);
     {
       std::vector<std::string> want;
       for (int l = 0; l < NL; ++l)
@@ -532,7 +573,7 @@ int main() {
     CHECK(llama_kv_cache_seq_len(C3, sa, &n) == LLAMA_OK && n == 20);  // advanced once
     CHECK(llama_kv_cache_free_blocks(C3, &n) == LLAMA_OK && n == 2);
     g_log.clear();
-    CHECK(llama_stack_decode(S, C3, 2, sids, x3, y3, LLAMA_DTYPE_F32, ws3, nullptr) == LLAMA_OK);
+    CHECK(llama_stack_decode(S, C3, 2, sids, x3, y3, LLAMA_DTYPE_F32, ws3, wsz, nullptr) == LLAMA_OK);
     CHECK(g_log.size() == NL * 8 + 1 && g_log.back() == "rms_final" && g_log[2] == "attn_decode");
     CHECK(g_attn_units == 2);  // two sequences of 21 keys
     CHECK(llama_kv_cache_seq_len(C3, sb, &n) == LLAMA_OK && n == 21);
@@ -564,7 +605,7 @@ int main() {
     }
     {
       CHECK(llama_layer_profile_enable(Ls[NL - 1], 1) == LLAMA_OK);
-      CHECK(llama_stack_decode(S, C3, 1, sids, x3, y3, LLAMA_DTYPE_F32, ws3, nullptr) == LLAMA_OK);
+      CHECK(llama_stack_decode(S, C3, 1, sids, x3, y3, LLAMA_DTYPE_F32, ws3, wsz, nullptr) == LLAMA_OK);
       llama_kernel_time kt[16];
       int32_t nk = 0;
       CHECK(llama_layer_profile_read(Ls[NL - 1], kt, 16, &nk, 1) == LLAMA_OK && nk == 9);

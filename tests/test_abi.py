@@ -115,8 +115,10 @@ def test_cache_bookkeeping_without_device(L):
 def test_forward_rejects_null_handles(L):
     lib = L.lib()
     ids = (ctypes.c_int32 * 1)(0)
-    assert lib.llama_layer_prefill(None, None, 1, 1, ids, None, None, 0, None, None) == -1
-    assert lib.llama_layer_decode(None, None, 1, ids, None, None, 0, None, None) == -1
+    assert lib.llama_layer_prefill(None, None, 1, 1, ids, None, None, 0, None, 0, None) == -1
+    assert lib.llama_layer_decode(None, None, 1, ids, None, None, 0, None, 0, None) == -1
+    assert lib.llama_stack_prefill(None, None, 1, 1, ids, None, None, 0, None, 0, None) == -1
+    assert lib.llama_stack_decode(None, None, 1, ids, None, None, 0, None, 0, None) == -1
 
 
 def test_binding_rejects_tensors_the_abi_would_misread(L):
