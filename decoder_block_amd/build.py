@@ -22,7 +22,8 @@ LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libllama_layer.so")
 
 ARCH = "gfx950"
-SOURCES = ["llama_layer.cpp", "gemm.hip", "norm.hip", "attn_prefill.hip", "attn_decode.hip", "misc.hip"]
+SOURCES = ["llama_layer.cpp", "gemm.hip", "norm.hip", "attn_prefill.hip", "attn_decode.hip", "misc.hip",
+           "scratch.hip"]
 # MFMA results in VGPRs (not AGPRs): the attention kernels rescale their output
 # accumulators with VALU ops, which cannot read AGPRs.
 EXTRA = {"attn_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],

@@ -142,6 +142,11 @@ hipError_t event_destroy(void* ev);
 hipError_t event_record(void* ev, hipStream_t s);
 hipError_t event_elapsed_ms(float* ms, void* start, void* stop);  // waits for `stop`
 
+// The calling thread's current device's copy of the library's static scratch
+// array (LLAMA_SCRATCH_BYTES bytes): its device address, looked up once per
+// device.
+hipError_t scratch_region(void** ptr, size_t* bytes);
+
 // Contiguous [n][G][D] <-> paged cache for positions start.. of one sequence.
 hipError_t launch_kv_copy(DType t, const CacheView& c, int seq, int start, int n, void* k,
                           void* v, bool to_cache, hipStream_t s);

@@ -412,6 +412,7 @@ const char* llama_status_string(llama_status s) {
     case LLAMA_ERR_POSITION: return "position beyond max_position";
     case LLAMA_ERR_HIP: return "HIP error";
     case LLAMA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LLAMA_ERR_SCRATCH: return "workspace larger than the static scratch buffer";
   }
   return "unknown status";
 }
@@ -1080,6 +1081,26 @@ llama_status llama_layer_decode(llama_layer* layer, llama_kv_cache* cache, int32
                                 const void* x, void* out, int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                 void* stream) {
   return forward(layer, cache, batch, 1, seq_ids, x, out, out_dtype, workspace, workspace_bytes, stream, true);
+}
+
+llama_status llama_layer_decode_noalloc(llama_layer* layer, llama_kv_cache* cache, int32_t batch,
+                                        const int32_t* seq_ids, const void* x, void* out, int32_t out_dtype,
+                                        void* stream) {
+  if (!layer) return LLAMA_ERR_INVALID_ARG;
+  // host validation first (a stand-in workspace address: only its presence
+  // and alignment are checked here)
+  llama_status st = check_call(layer->s, cache, batch, 1, seq_ids, x, out, out_dtype, reinterpret_cast<void*>(256));
+  if (st != LLAMA_OK) return st;
+  if (ws_layout(layer->s, (size_t)batch, (size_t)batch).total > LLAMA_SCRATCH_BYTES) return LLAMA_ERR_SCRATCH;
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  HIP_TRY(llk::scratch_region(&scratch, &scratch_bytes));
+  // no timing events for this call: creating them may allocate
+  const bool prof = layer->profiling;
+  layer->profiling = false;
+  st = forward(layer, cache, batch, 1, seq_ids, x, out, out_dtype, scratch, scratch_bytes, stream, true);
+  layer->profiling = prof;
+  return st;
 }
 
 }  // extern "C"

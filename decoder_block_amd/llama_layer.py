@@ -23,7 +23,7 @@ LLAMA_DTYPE_BF16 = 1
 
 STATUS = {0: "LLAMA_OK", -1: "LLAMA_ERR_INVALID_ARG", -2: "LLAMA_ERR_SHAPE", -3: "LLAMA_ERR_DTYPE",
           -4: "LLAMA_ERR_CACHE_FULL", -5: "LLAMA_ERR_BAD_SEQ", -6: "LLAMA_ERR_POSITION",
-          -7: "LLAMA_ERR_HIP", -8: "LLAMA_ERR_UNSUPPORTED"}
+          -7: "LLAMA_ERR_HIP", -8: "LLAMA_ERR_UNSUPPORTED", -9: "LLAMA_ERR_SCRATCH"}
 
 EXPORTED = ("llama_status_string", "llama_layer_packed_bytes", "llama_layer_create",
             "llama_layer_workspace_bytes", "llama_layer_destroy", "llama_kv_cache_bytes",
@@ -32,7 +32,11 @@ EXPORTED = ("llama_status_string", "llama_layer_packed_bytes", "llama_layer_crea
             "llama_kv_cache_write", "llama_kv_cache_read", "llama_layer_prefill", "llama_layer_decode",
             "llama_layer_profile_enable", "llama_layer_profile_read", "llama_kv_cache_bytes_layers",
             "llama_kv_cache_create_layers", "llama_kv_cache_num_layers", "llama_stack_create",
-            "llama_stack_workspace_bytes", "llama_stack_destroy", "llama_stack_prefill", "llama_stack_decode")
+            "llama_stack_workspace_bytes", "llama_stack_destroy", "llama_stack_prefill", "llama_stack_decode",
+            "llama_layer_decode_noalloc")
+
+# bytes of the library's static scratch buffer (LLAMA_SCRATCH_BYTES in the header)
+SCRATCH_BYTES = 64 << 20
 
 
 class LlamaError(RuntimeError):
@@ -99,6 +103,7 @@ def lib() -> ctypes.CDLL:
         "llama_stack_destroy": (ctypes.c_int, [P]),
         "llama_stack_prefill": (ctypes.c_int, [P, P, I32, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, SZ, P]),
         "llama_stack_decode": (ctypes.c_int, [P, P, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P, SZ, P]),
+        "llama_layer_decode_noalloc": (ctypes.c_int, [P, P, I32, ctypes.POINTER(I32), P, P, ctypes.c_int, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -300,6 +305,12 @@ def llama_layer_decode(layer, cache, batch: int, seq_ids, x, out, out_dtype: int
     _check(lib().llama_layer_decode(layer, cache, batch, _i32_array(seq_ids), _ptr(x), _ptr(out), out_dtype,
                                     _ptr(workspace), _nbytes(workspace, workspace_bytes), _stream(stream)),
            "llama_layer_decode")
+
+
+def llama_layer_decode_noalloc(layer, cache, batch: int, seq_ids, x, out, out_dtype: int, stream=None):
+    """llama_layer_decode with the library's static scratch buffer as workspace (allocates nothing)."""
+    _check(lib().llama_layer_decode_noalloc(layer, cache, batch, _i32_array(seq_ids), _ptr(x), _ptr(out), out_dtype,
+                                            _stream(stream)), "llama_layer_decode_noalloc")
 
 
 def llama_layer_profile_enable(layer, enable: bool):

@@ -76,7 +76,8 @@ typedef enum {
   LLAMA_ERR_BAD_SEQ = -5,     /* unknown or duplicated seq_id */
   LLAMA_ERR_POSITION = -6,    /* a position would reach max_position */
   LLAMA_ERR_HIP = -7,         /* a HIP call or kernel launch failed */
-  LLAMA_ERR_UNSUPPORTED = -8  /* valid but not supported by this build */
+  LLAMA_ERR_UNSUPPORTED = -8, /* valid but not supported by this build */
+  LLAMA_ERR_SCRATCH = -9      /* the call needs more than the static scratch buffer holds */
 } llama_status;
 
 typedef enum { LLAMA_DTYPE_F32 = 0, LLAMA_DTYPE_BF16 = 1 } llama_dtype;
@@ -229,6 +230,29 @@ llama_status llama_layer_decode(llama_layer* layer, llama_kv_cache* cache, int32
                                 const int32_t* seq_ids, const void* x, void* out,
                                 int32_t out_dtype, void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/* ---- decode without allocation ---------------------------------------- */
+
+/* Bytes of the static device scratch buffer behind llama_layer_decode_noalloc. */
+#define LLAMA_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * llama_layer_decode with the workspace taken from a static device array of
+ * LLAMA_SCRATCH_BYTES bytes inside the library, of which every GPU the
+ * library runs on holds one copy until the process ends.  Arguments,
+ * results, bookkeeping and errors are those of llama_layer_decode; a call
+ * whose workspace (llama_layer_workspace_bytes(batch, batch)) exceeds
+ * LLAMA_SCRATCH_BYTES returns LLAMA_ERR_SCRATCH before any device work.  The
+ * call allocates nothing (no hipMalloc, no events: per-kernel timing is not
+ * recorded for it); on the first call on a device it looks up that device's
+ * copy of the array.  Every call on a GPU shares that GPU's copy: calls that
+ * overlap in time on one GPU (other streams, other threads) race and must be
+ * serialised by the caller.  No kernel needs the buffer cleared: each call
+ * writes every scratch byte it reads before reading it. */
+llama_status llama_layer_decode_noalloc(llama_layer* layer, llama_kv_cache* cache, int32_t batch,
+                                        const int32_t* seq_ids, const void* x, void* out,
+                                        int32_t out_dtype, void* stream);
 
 /* ---- stack of layers + final RMSNorm ---------------------------------- */
 

@@ -34,6 +34,9 @@ struct FinalCall { const void* gamma; void* y; };
 static FinalCall g_final = {nullptr, nullptr};
 // name of a stubbed launch that fails (empty: none), to test the rollback of a failed call
 static std::string g_fail_launch;
+// the static scratch buffer: a host allocation here, looked up on every call
+static void* g_scratch = nullptr;
+static int g_scratch_lookups = 0;
 static bool fails(const char* what) { return g_fail_launch == what; }
 
 namespace llk {
@@ -126,6 +129,13 @@ hipError_t launch_zero(void* dst, size_t bytes, hipStream_t) {
 hipError_t launch_upload(const Upload& u, hipStream_t) {
   for (int i = 0; i < u.n; ++i) u.base[(u.idx[i] >> 31) & 1][u.idx[i] & 0x7fffffff] = u.val[i];
   ++g_uploads;
+  return hipSuccess;
+}
+hipError_t scratch_region(void** ptr, size_t* bytes) {
+  if (!g_scratch && posix_memalign(&g_scratch, 256, LLAMA_SCRATCH_BYTES) != 0) return hipErrorOutOfMemory;
+  ++g_scratch_lookups;
+  *ptr = g_scratch;
+  *bytes = LLAMA_SCRATCH_BYTES;
   return hipSuccess;
 }
 hipError_t copy_to_device(void* dst, const void* src, size_t bytes, hipStream_t) {
@@ -383,6 +393,35 @@ int main() {
     CHECK(desc[1] == 34);
   }
 
+  // decode without allocation: the workspace is the static scratch buffer
+  {
+    g_log.clear();
+    const int lookups = g_scratch_lookups;
+    CHECK(llama_layer_decode_noalloc(L, C, 1, ids, x, out, LLAMA_DTYPE_F32, nullptr) == LLAMA_OK);
+    CHECK(g_scratch_lookups == lookups + 1 && g_scratch != nullptr);
+    CHECK(g_log.size() == 8 && g_log[2] == "attn_decode");
+    const int32_t* sdesc = (const int32_t*)g_scratch;
+    CHECK(sdesc[0] == s0 && sdesc[1] == 35);
+    CHECK(llama_kv_cache_seq_len(C, s0, &n) == LLAMA_OK && n == 36);
+    // validation comes first: nothing is looked up or launched for a bad call
+    g_log.clear();
+    CHECK(llama_layer_decode_noalloc(L, C, 1, ids, nullptr, out, LLAMA_DTYPE_F32, nullptr) == LLAMA_ERR_INVALID_ARG);
+    CHECK(llama_layer_decode_noalloc(L, C, 1, ids, x, out, LLAMA_DTYPE_BF16, nullptr) == LLAMA_ERR_DTYPE);
+    CHECK(llama_layer_decode_noalloc(nullptr, C, 1, ids, x, out, LLAMA_DTYPE_F32, nullptr) == LLAMA_ERR_INVALID_ARG);
+    // a batch whose workspace exceeds the buffer is refused before any HIP call
+    size_t big = 0;
+    int32_t bigb = 1;
+    while (llama_layer_workspace_bytes(L, bigb, bigb, &big) == LLAMA_OK && big <= LLAMA_SCRATCH_BYTES) bigb *= 2;
+    CHECK(big > LLAMA_SCRATCH_BYTES);
+    std::vector<int32_t> many(bigb, s0);
+    void* xb = aligned_buf((size_t)bigb * 256 * 4);
+    CHECK(llama_layer_decode_noalloc(L, C, bigb, many.data(), xb, xb, LLAMA_DTYPE_F32, nullptr) == LLAMA_ERR_SCRATCH);
+    std::free(xb);
+    CHECK(g_log.empty() && g_scratch_lookups == lookups + 1);
+    CHECK(llama_kv_cache_seq_len(C, s0, &n) == LLAMA_OK && n == 36);
+    CHECK(std::string(llama_status_string(LLAMA_ERR_SCRATCH)).find("scratch") != std::string::npos);
+  }
+
   // per-kernel timing: two events per launch, totals per kernel family
   {
     CHECK(llama_layer_profile_enable(L, 1) == LLAMA_OK);
@@ -630,6 +669,7 @@ int main() {
   std::free(out);
   std::free(packed);
   for (void* p : wbufs) std::free(p);
+  std::free(g_scratch);
   if (g_fail) {
     std::fprintf(stderr, "%d checks failed\n", g_fail);
     return 1;
