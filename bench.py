@@ -130,17 +130,24 @@ def run_prefill(args, torch, L, synth):
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    profile_all(L, layers, True)
+    # timed steps without per-kernel events ...
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    # ... then the same number of steps again with HIP events around every
+    # launch on the layer's stream, for the per-kernel breakdown
+    profile_all(L, layers, True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
     prof = profile_sum(L, layers)
     profile_all(L, layers, False)
-    ms = (t1 - t0) * 1e3 / args.steps
+    ms_prof = (t2 - t1) * 1e3 / args.steps
     flops = {k: v * nl for k, v in prefill_flops(w).items()}
     kern = {}
     for name, (n, tot) in prof.items():
@@ -154,13 +161,20 @@ def run_prefill(args, torch, L, synth):
     total_flops = sum(flops.values())
     rec = traffic_record(dom)
     traffic = int(rec["bytes_per_launch"]) if rec and "bytes_per_launch" in rec else None
-    log(f"[bench] prefill {ms:.3f} ms/step, layer {total_flops / ms / 1e9:.1f} TFLOP/s")
+    log(f"[bench] prefill {ms:.3f} ms/step ({ms_prof:.3f} with per-kernel events), "
+        f"layer {total_flops / ms / 1e9:.1f} TFLOP/s")
+    layer_ach = total_flops / (ms * 1e-3) / 1e12
     res = {
-        "tokens_per_s": w.batch * w.seq_len / (ms * 1e-3), "ms": ms, "kernels": kern,
-        "layer_tflops": total_flops / (ms * 1e-3) / 1e12,
+        "tokens_per_s": w.batch * w.seq_len / (ms * 1e-3), "ms": ms, "ms_profiled": ms_prof, "kernels": kern,
+        "layer_tflops": layer_ach,
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "flops_per_launch": flops[dom] // nl, "avg_launch_ms": round(dom_ms, 4)},
+        # the whole layer against the same peak: every kernel's algorithmic flops
+        # over the wall-clock step time (norms and launch gaps included)
+        "layer_roofline": {"bound": "mfma", "achieved": round(layer_ach, 1), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(layer_ach / PEAK_BF16_TFLOPS, 4),
+                           "flops_per_step": total_flops},
     }
     cache.close()
     model.close()
@@ -233,6 +247,16 @@ def run_decode(args, torch, L, synth):
                if rec and "ratio_to_algorithmic" in rec else None)
     kern = {n: {"avg_us": round(t / c * 1e3, 2), "launches": c} for n, (c, t) in prof.items()}
     step_bytes = kv_bytes + weight_bytes
+    # decode attention plus the norms: their kernels' summed event time per
+    # step against their algorithmic bytes (K/V once per group, q in, attention
+    # out; the norms read x (bf16) and h (fp32) and write the bf16 operands)
+    T = w.batch
+    an_kernels = [k for k in ("attn_decode_split", "attn_decode_combine", "rms_rowscale", "rms_convert")
+                  if k in prof]
+    an_us = sum(prof[k][1] / prof[k][0] * 1e3 for k in an_kernels)
+    an_bytes = (kv_bytes_prof + 2 * T * H * D * 2            # K/V, q, attention output
+                + T * d * 2 * 2 + T * d * 4 + T * d * 2)     # norm 1 (x in, operand out), norm 2 (h in, operand out)
+    an_ach = an_bytes / (an_us * 1e-6) / 1e9
     log(f"[bench] decode {us:.1f} us/step ({us_prof:.1f} with per-kernel events), "
         f"{step_bytes / (us * 1e-6) / 1e9:.0f} GB/s whole step")
     res = {
@@ -240,6 +264,9 @@ def run_decode(args, torch, L, synth):
         "us_per_step_profiled": round(us_prof, 2),
         "mean_context": float(np.mean(ctx_start)), "kernels": kern,
         "step_hbm_frac": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "attn_norms_roofline": {"bound": "hbm", "kernels": an_kernels, "achieved": round(an_ach, 1),
+                                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(an_ach / PEAK_HBM_GBS, 4),
+                                "bytes_per_step": an_bytes, "us_per_step": round(an_us, 2)},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": kv_bytes_prof, "avg_launch_ms": round(dom_ms, 4)},
@@ -251,20 +278,35 @@ def run_decode(args, torch, L, synth):
     return res
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(synth, w, n_rows: int):
-    """The float64 oracle on the prefill workload, or on a row sample of it (host cores)."""
+    """The float64 oracle on the prefill workload, or on a row sample of it (host cores).
+
+    The oracle's work is numpy matmuls; `cores` is the thread count of the BLAS
+    pool that runs them (OMP_NUM_THREADS where set), `host_logical_cpus` what
+    the host reports."""
     import oracle
     from threadpoolctl import threadpool_info
     ws = synth.layer_weights(w)
     wo = {k: synth.as_f64(v) for k, v in ws.items()}
     x = synth.as_f64(synth.layer_input(w))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    host = {"host_logical_cpus": os.cpu_count(), "cpu_model": cpu_model()}
     if n_rows >= w.seq_len:
         t0 = time.perf_counter()
         oracle.prefill(w.config_dict(), wo, x)
         t = time.perf_counter() - t0
         return {"value": round(w.batch * w.seq_len / t, 2), "unit": "tokens/s", "cores": int(threads),
-                "kind": "oracle",
+                "kind": "oracle", **host,
                 "sample": f"{w.name}: the whole layer prefill (B {w.batch}, S {w.seq_len}) in float64, {t:.1f} s"}
     rows = np.unique(np.linspace(0, w.seq_len - 1, n_rows).astype(np.int64))
     t0 = time.perf_counter()
@@ -275,7 +317,7 @@ def cpu_baseline(synth, w, n_rows: int):
     t_kv = t1 - t0                                 # K/V of all tokens + one row
     t_full = t_kv + (t2 - t1 - t_kv) * (w.seq_len / len(rows))
     return {"value": round(w.batch * w.seq_len / t_full, 2), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", **host,
             "sample": (f"{w.name}: K/V of all {w.seq_len} tokens plus outputs of {len(rows)} evenly spaced "
                        f"rows, float64; {t2 - t0:.1f} s measured, full-layer time extrapolated linearly "
                        f"in rows")}
@@ -327,6 +369,7 @@ def main():
         "layer_tflops": round(pre["layer_tflops"], 1),
         "layer_mfma_frac": round(pre["layer_tflops"] / PEAK_BF16_TFLOPS, 4),
         "roofline": pre["roofline"],
+        "layer_roofline": pre["layer_roofline"],
         "kernels": pre["kernels"],
         "decode": dec,
         "cpu_baseline": cpu,
