@@ -230,16 +230,24 @@ def decode_step(cfg: dict, w: dict, x: np.ndarray, caches: list):
     """One decode step for B sequences: x [B, d]; caches[b] = (K [len_b,G,D], V).
 
     The new token of sequence b sits at position len_b, is appended to its
-    cache, and attends to all len_b + 1 keys ([P3] sections 3 and 7).
-    Returns (out [B, d], list of updated (K, V)).
+    cache, and attends to all len_b + 1 keys ([P3] sections 3 and 7).  The
+    projections, the norms and the MLP act on each row alone, so they are
+    applied to the B rows at once; attention runs per sequence over its own
+    cache.  Returns (out [B, d], list of updated (K, V)).
     """
-    outs, new = [], []
-    for b in range(x.shape[0]):
-        pk, pv = caches[b]
-        o, k, v = layer_forward(cfg, w, x[b:b + 1], pk.shape[0], pk, pv)
-        outs.append(o[0])
-        new.append((np.concatenate([pk, k]), np.concatenate([pv, v])))
-    return np.stack(outs), new
+    B = x.shape[0]
+    H = cfg["num_attention_heads"]
+    pos = np.array([c[0].shape[0] for c in caches], dtype=np.int64)
+    k_new, v_new = project_kv(cfg, w, x, pos)
+    new = [(np.concatenate([pk, k_new[b:b + 1]]), np.concatenate([pv, v_new[b:b + 1]]))
+           for b, (pk, pv) in enumerate(caches)]
+    n1 = rms_norm(x, w["input_layernorm"], cfg["rms_norm_eps"])
+    q = apply_rope(_split_heads(linear(n1, w["q_proj"]), H), pos, cfg["rope_theta"],
+                   cfg.get("rope_style", "interleaved"))
+    a = np.stack([causal_gqa_attention(q[b:b + 1], new[b][0], new[b][1], pos[b:b + 1],
+                                       np.arange(pos[b] + 1))[0] for b in range(B)])
+    h = x + linear(a.reshape(B, -1), w["o_proj"])
+    return mlp_block(cfg, w, h), new
 
 
 # ----------------------------------------------------------------------------

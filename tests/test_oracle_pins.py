@@ -438,6 +438,26 @@ def test_decode_equals_full_recompute():
     np.testing.assert_allclose(caches[0][0], kf[0], rtol=1e-12, atol=1e-12)
 
 
+def test_batched_decode_of_ragged_sequences_equals_full_recompute():
+    # three sequences at different lengths decode together for three steps;
+    # each step of each sequence equals its own full causal recompute
+    cfg = _tiny_cfg(H=4, G=2)
+    w = _tiny_weights(cfg, seed=3)
+    lens, steps = [1, 6, 11], 3
+    xs = [rng.standard_normal((n + steps, 32)) for n in lens]
+    caches = []
+    for b, n in enumerate(lens):
+        _, k, v = oracle.layer_forward(cfg, w, xs[b][:n])
+        caches.append((k, v))
+    for t in range(steps):
+        xt = np.stack([xs[b][lens[b] + t] for b in range(3)])
+        o, caches = oracle.decode_step(cfg, w, xt, caches)
+        for b, n in enumerate(lens):
+            full, _, _ = oracle.layer_forward(cfg, w, xs[b][:n + t + 1])
+            np.testing.assert_allclose(o[b], full[-1], rtol=1e-12, atol=1e-12)
+    assert [c[0].shape[0] for c in caches] == [n + steps for n in lens]
+
+
 def test_subset_rows_equal_full_rows():
     cfg = _tiny_cfg()
     w = _tiny_weights(cfg)
