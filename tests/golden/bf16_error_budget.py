@@ -1,0 +1,128 @@
+"""Write tests/golden/bf16_error_budget.json: the error that the bf16 kernels'
+storage roundings cause, predicted by tests/bf16_model.py against the float64
+oracle on the exact inputs of the GPU parity cases that the workload
+definitions give no tolerance for, plus the single layers they build on.
+
+    python -m tests.golden.bf16_error_budget [--only NAME ...]
+
+Calls only the oracle, the rounding model and the seeded input generators;
+nothing here touches the GPU path.  Errors are those of tests/parity.py
+(divided by the RMS of the oracle output).  The tolerances derived from these
+predictions are in tests/parity.py.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from decoder_block_amd import synth  # noqa: E402
+from tests import bf16_model as M  # noqa: E402
+
+OUT = os.path.join(ROOT, "tests", "golden", "bf16_error_budget.json")
+W = synth.WORKLOADS
+
+
+def errors(got, ref) -> dict:
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
+    rms = float(np.sqrt(np.mean(np.asarray(ref, np.float64) ** 2)))
+    return {"max_rel": float(d.max()) / rms, "mean_rel": float(d.mean()) / rms}
+
+
+def _weights(w, gamma_std=None, layer=0):
+    ws = synth.layer_weights(w, gamma_std, layer=layer)
+    return {k: synth.as_f64(v) for k, v in ws.items()}
+
+
+def stack3(_):
+    """The bf16 stack case: LLaMA-3-8B shape, B 2, S 300, 3 layers, prefill + 2 decode steps."""
+    w = synth.scaled(W[3], batch=2, seq_len=300)
+    cfg = w.config_dict()
+    NL = 3
+    wo = [_weights(w, None, l) for l in range(NL)]
+    gf = synth.as_f64(synth.final_norm_weight(w))
+    x = synth.as_f64(synth.layer_input(w))
+    res = {"case": "llama3-8b shape, B 2, S 300, 3 layers (prefill f32 out, 2 decode steps bf16 out)"}
+    ref, k_ref, v_ref = oracle.stack_prefill(cfg, wo, gf, x, "bf16")
+    got, k_m, v_m = M.stack_prefill(cfg, wo, gf, x)
+    res["prefill"] = errors(got, ref)
+    res["last_layer_k"] = errors(k_m[NL - 1, 1], k_ref[NL - 1, 1])
+    res["last_layer_v"] = errors(v_m[NL - 1, 1], v_ref[NL - 1, 1])
+    # a single layer on the same input (the first layer of the stack)
+    o1, _, _ = oracle.prefill(cfg, wo[0], x)
+    m1, _, _ = M.prefill(cfg, wo[0], x)
+    res["single_layer_prefill"] = errors(m1, o1)
+    c_ref = [[(k_ref[l, b], v_ref[l, b]) for b in range(w.batch)] for l in range(NL)]
+    c_m = [[(k_m[l, b], v_m[l, b]) for b in range(w.batch)] for l in range(NL)]
+    for step in range(2):
+        xt = synth.as_f64(synth.decode_input(w, step))
+        r, c_ref = oracle.stack_decode_step(cfg, wo, gf, xt, c_ref, "bf16")
+        g, c_m = M.stack_decode_step(cfg, wo, gf, xt, c_m, out_bf16=True)
+        res[f"decode_step{step}"] = errors(g, r)
+    return res
+
+
+def gamma_rows(args):
+    """gamma ~ 1 + N(0, 0.1^2), LLaMA-3-8B shape, B 1, by sequence length (row samples past S 300)."""
+    out = {}
+    for S in args.gamma_lengths:
+        w = synth.scaled(W[3], batch=1, seq_len=S)
+        cfg = w.config_dict()
+        x = synth.as_f64(synth.layer_input(w))
+        rows = None if S <= 300 else synth.sample_rows(w, S, n_random=448, edge=64)
+        ent = {"rows": "all" if rows is None else f"{len(rows)} sampled (first/last 64 + 448 seeded)"}
+        for tag, gstd in (("gamma", 0.1), ("gamma_one", None)):
+            wo = _weights(w, gstd)
+            ref, _, _ = oracle.prefill(cfg, wo, x, rows=rows)
+            got, _, _ = M.prefill(cfg, wo, x, rows=rows)
+            ent[tag] = errors(got, ref)
+        out[str(S)] = ent
+        print("gamma", S, ent, flush=True)
+    return out
+
+
+def short_prompts(_):
+    """gamma = 1 prompts shorter than the workloads': LLaMA-3-8B shape, B 3, S 77 and B 1, S 16."""
+    out = {}
+    for B, S in ((3, 77), (1, 16)):
+        w = synth.scaled(W[3], batch=B, seq_len=S)
+        cfg = w.config_dict()
+        wo = _weights(w)
+        x = synth.as_f64(synth.layer_input(w))
+        ref, _, _ = oracle.prefill(cfg, wo, x)
+        got, _, _ = M.prefill(cfg, wo, x)
+        out[f"B{B}_S{S}"] = errors(got, ref)
+        print("short", B, S, out[f"B{B}_S{S}"], flush=True)
+    return out
+
+
+PARTS = {"stack3": stack3, "gamma_by_length": gamma_rows, "short_prompts": short_prompts}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--only", nargs="*", choices=sorted(PARTS))
+    ap.add_argument("--gamma-lengths", nargs="*", type=int, default=[300, 500, 700, 1000, 2048, 4096, 8192])
+    args = ap.parse_args()
+    data = json.load(open(OUT)) if os.path.exists(OUT) else {}
+    data["about"] = ("errors of tests/bf16_model.py (bf16 storage roundings of the bf16 kernels) against the "
+                     "float64 oracle on the GPU parity cases' inputs; max/mean |diff| / RMS(oracle)")
+    for name in args.only or sorted(PARTS):
+        t0 = time.time()
+        data[name] = PARTS[name](args)
+        print(name, f"{time.time() - t0:.0f} s", json.dumps(data[name]), flush=True)
+        with open(OUT, "w") as f:
+            json.dump(data, f, indent=1, sort_keys=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -3,6 +3,8 @@ library on seeded workloads and compare with the float64 oracle."""
 from __future__ import annotations
 
 import functools
+import json
+import os
 
 import numpy as np
 import torch
@@ -13,29 +15,39 @@ from decoder_block_amd import synth
 # Tolerances, errors divided by the RMS of the oracle output ("unit-scale"):
 #   fp32 layer: max |gpu - oracle| / RMS <= 1e-4
 #   bf16 layer: max <= 3e-2 and mean <= 3e-3
-TOL = {"f32": {"max_rel": 1e-4}, "bf16": {"max_rel": 3e-2, "mean_rel": 3e-3},
-       # gamma != 1 (a parity-only case beyond the workloads, whose gammas are 1):
-       # gamma_1 folded into W_qkv adds one bf16 rounding of the q/k/v weights,
-       # worth about 1.7e-3 in quadrature on top of the ~2.8e-3 of the gamma = 1
-       # layer at 300 tokens
-       "bf16_gamma": {"max_rel": 3e-2, "mean_rel": 4e-3}}
+TOL = {"f32": {"max_rel": 1e-4}, "bf16": {"max_rel": 3e-2, "mean_rel": 3e-3}}
+
+# Cases the workload definitions give no tolerance for (a stack of layers,
+# gamma != 1, prompts shorter than the workloads') are held to the error that
+# the bf16 kernels' storage roundings cause on that case's own inputs, as
+# predicted by tests/bf16_model.py (the oracle with a bf16 rounding at each
+# point where the kernels store bf16, float64 everywhere else) and recorded in
+# tests/golden/bf16_error_budget.json by tests/golden/bf16_error_budget.py,
+# times a margin for what the model leaves out: fp32 accumulation order, the
+# hardware exp2 and reciprocal, the fp32 RoPE table.  On every case measured on
+# the GPU (single layers at S 300 and 8192 with gamma = 1 and gamma != 1, the
+# 3-layer stack) the GPU's mean error is within 2% of the model's and its max
+# within 8%; the margins are 10% on the mean and 30% on the max (the max is one
+# extreme element, the mean averages millions).
+BUDGET_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "bf16_error_budget.json")
+MODEL_MARGIN = {"mean_rel": 1.10, "max_rel": 1.30}
 
 
-def stack_tol(dtype: str, n_layers: int) -> str:
-    """Tolerance key of an n-layer stack compared at its output.
+@functools.lru_cache(maxsize=None)
+def _budget() -> dict:
+    with open(BUDGET_FILE) as f:
+        return json.load(f)
 
-    Each layer adds an error within the single-layer limits (its own bf16
-    roundings), and the error already in its input reaches its output through
-    the residual path with gain about one; the final RMSNorm rescales the
-    output to unit RMS, which keeps the errors relative.  Summing the n
-    contributions (triangle inequality) scales the single-layer limits by n.
-    (Independent contributions would add in quadrature, sqrt(n); a 3-layer
-    LLaMA-3-8B-shaped stack at 300 tokens measures about 2.1 times the
-    single-layer mean error, between the two.)
-    """
-    key = f"{dtype}_stack{n_layers}"
+
+def model_tol(path: str) -> str:
+    """Tolerance key for the case at `path` ("part/case/.../errors") of the error
+    budget: the model's max and mean errors times MODEL_MARGIN."""
+    key = "model:" + path
     if key not in TOL:
-        TOL[key] = {k: v * n_layers for k, v in TOL[dtype].items()}
+        e = _budget()
+        for part in path.split("/"):
+            e = e[part]
+        TOL[key] = {k: e[k] * m for k, m in MODEL_MARGIN.items()}
     return key
 
 

@@ -92,7 +92,7 @@ def test_bf16_prefill_small(name):
 # full-size prefill workloads, compared on a seeded sample of rows
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("wid,n_random,edge", [(2, 448, 64), (3, 448, 64), (5, 96, 16)])
+@pytest.mark.parametrize("wid,n_random,edge", [(2, 448, 64), (3, 448, 64), (5, 448, 64)])
 def test_bf16_prefill_full_size_sampled_rows(wid, n_random, edge):
     w = W[wid]
     rows = synth.sample_rows(w, w.seq_len, n_random=n_random, edge=edge)
@@ -105,12 +105,13 @@ def test_bf16_prefill_full_size_sampled_rows(wid, n_random, edge):
 # batched decode over a paged cache pre-filled with N(0,1) keys/values
 # ----------------------------------------------------------------------------
 
-def _decode_setup(w, n_seqs=None, lens=None, block_seed=None, max_position=None):
+def _decode_setup(w, n_seqs=None, lens=None, block_seed=None, max_position=None, steps=None):
     ws, wo = P.weights_for(w)
-    layer = P.make_layer(w, ws, max_position)
+    steps = w.decode_steps if steps is None else steps
+    layer = P.make_layer(w, ws, max_position or (w.ctx_hi + steps + 1 if lens is None else None))
     lens = synth.context_lengths(w) if lens is None else np.asarray(lens)
     B = len(lens)
-    nb = int(sum((l + w.decode_steps + 15) // 16 for l in lens))
+    nb = int(sum((l + steps + 15) // 16 for l in lens))
     from decoder_block_amd.llama_layer import PagedKVCache
     order = None
     if block_seed is not None:
@@ -127,18 +128,26 @@ def _decode_setup(w, n_seqs=None, lens=None, block_seed=None, max_position=None)
     return layer, cache, sids, host, wo
 
 
-def test_decode_llama3_8b_batch64_two_steps():
+@pytest.mark.timeout(900)
+def test_decode_llama3_8b_batch64_33_steps():
+    # the decode workload (B 64, contexts U[512, 8192]) over 33 consecutive
+    # steps, each compared with the oracle: every sequence crosses at least two
+    # 16-token block boundaries, so blocks are allocated mid-decode
     w = W[4]
-    layer, cache, sids, host, wo = _decode_setup(w)
-    for step in range(2):
+    layer, cache, sids, host, wo = _decode_setup(w, steps=33)
+    lens0 = [cache.seq_len(s) for s in sids]
+    worst = {"max_rel": 0.0, "mean_rel": 0.0}
+    for step in range(33):
         xt = synth.decode_input(w, step)
         o = layer.decode(cache, sids, xt.cuda())
         torch.cuda.synchronize()
         ref, host = oracle.decode_step(_cfg(w), wo, synth.as_f64(xt), host)
         e = P.assert_close(P.to_np(o), ref, "bf16", f"decode step {step}")
-        print("decode step", step, e)
-    for b in (0, 17, 63):
-        assert cache.seq_len(sids[b]) == len(host[b][0])
+        worst = {k: max(worst[k], e[k]) for k in worst}
+    print("decode B=64, 33 steps, worst step", worst)
+    for b in range(w.batch):
+        assert cache.seq_len(sids[b]) == len(host[b][0]) == lens0[b] + 33
+        assert (lens0[b] + 33 + 15) // 16 - (lens0[b] + 15) // 16 >= 2
 
 
 def test_decode_ragged_lengths_and_group_ratios():
@@ -229,11 +238,35 @@ def test_decode_matches_full_recompute_and_continuation_prefill():
     assert torch.equal(p1, full[:, :180])
 
 
-def test_random_gammas_bf16():
+def test_random_gammas_bf16_full_size_sampled_rows():
+    # gamma ~ 1 + N(0, 0.1^2) at the LLaMA-3-8B workload size (B 1, S 8192),
+    # compared on the seeded row sample at the workloads' bf16 limits
+    w = W[3]
+    rows = synth.sample_rows(w, w.seq_len, n_random=448, edge=64)
+    got, ref, _ = _prefill_case(w, rows=rows, gamma_std=0.1)
+    e = P.assert_close(got, ref, "bf16", "gamma ~ 1 + N(0, 0.1^2), S 8192")
+    print("random gammas, S 8192", len(rows), "rows", e)
+
+
+def test_random_gammas_bf16_300_tokens():
+    # the same gammas at 300 tokens: folding gamma_1 into the q/k/v weights adds
+    # one bf16 rounding of them, and at this length the error exceeds the
+    # workloads' 3e-3 mean limit; held to what the rounding placement predicts
     w = synth.scaled(W[3], batch=1, seq_len=300)
     got, ref, _ = _prefill_case(w, gamma_std=0.1)
-    e = P.assert_close(got, ref, "bf16_gamma", "gamma ~ 1 + N(0, 0.1^2)")
-    print("random gammas", e)
+    e = P.assert_close(got, ref, P.model_tol("gamma_by_length/300/gamma"), "gamma ~ 1 + N(0, 0.1^2), S 300")
+    print("random gammas, S 300", e)
+
+
+@pytest.mark.parametrize("B,S", [(3, 77), (1, 16)])
+def test_bf16_short_prompts(B, S):
+    # prompts shorter than the workloads': with few keys per query, attention
+    # averages out less of the q/k/v rounding; held to what the rounding
+    # placement predicts for these inputs (B 3 S 77 sits just above 3e-3)
+    w = synth.scaled(W[3], batch=B, seq_len=S)
+    got, ref, _ = _prefill_case(w, block_seed=B + S)
+    e = P.assert_close(got, ref, P.model_tol(f"short_prompts/B{B}_S{S}"), f"short prompt B {B} S {S}")
+    print("short prompt", B, S, e)
 
 
 def test_cache_restore_gives_identical_decode():

@@ -2,8 +2,9 @@
 then the final RMSNorm) against the float64 stack oracle.
 
 The oracle rounds the hidden state to the storage dtype between layers, as
-the stack holds it; the tolerances of a stack are those of one layer, scaled
-as derived in tests/parity.py.
+the stack holds it.  The bf16 stack is held to the error its storage roundings
+cause on these inputs (tests/parity.py model_tol; the workloads define no
+tolerance for a stack).
 """
 import numpy as np
 import pytest
@@ -66,18 +67,18 @@ def test_bf16_stack_prefill_and_decode():
     y = stack.prefill(cache, sids, x.cuda())
     torch.cuda.synchronize()
     ref, k_ref, v_ref = oracle.stack_prefill(w.config_dict(), wo, gf, synth.as_f64(x), "bf16")
-    e = P.assert_close(P.to_np(y), ref, P.stack_tol("bf16", NL), "bf16 stack prefill")
+    e = P.assert_close(P.to_np(y), ref, P.model_tol("stack3/prefill"), "bf16 stack prefill")
     print("bf16 stack prefill", e)
     k, v = cache.read(sids[1], 0, w.seq_len)
-    P.assert_close(P.to_np(k[NL - 1]), k_ref[NL - 1, 1], P.stack_tol("bf16", NL - 1), "last layer cached K")
-    P.assert_close(P.to_np(v[NL - 1]), v_ref[NL - 1, 1], P.stack_tol("bf16", NL - 1), "last layer cached V")
+    P.assert_close(P.to_np(k[NL - 1]), k_ref[NL - 1, 1], P.model_tol("stack3/last_layer_k"), "last layer cached K")
+    P.assert_close(P.to_np(v[NL - 1]), v_ref[NL - 1, 1], P.model_tol("stack3/last_layer_v"), "last layer cached V")
     caches = [[(k_ref[l, b], v_ref[l, b]) for b in range(w.batch)] for l in range(NL)]
     for step in range(2):
         xt = synth.decode_input(w, step)
         o = stack.decode(cache, sids, xt.cuda(), out_dtype="bf16")
         torch.cuda.synchronize()
         r, caches = oracle.stack_decode_step(w.config_dict(), wo, gf, synth.as_f64(xt), caches, "bf16")
-        e = P.assert_close(P.to_np(o), r, P.stack_tol("bf16", NL), f"bf16 stack decode step {step}")
+        e = P.assert_close(P.to_np(o), r, P.model_tol(f"stack3/decode_step{step}"), f"bf16 stack decode step {step}")
         print("bf16 stack decode", step, e)
 
 
