@@ -247,15 +247,18 @@ def run_decode(args, torch, L, synth):
                if rec and "ratio_to_algorithmic" in rec else None)
     kern = {n: {"avg_us": round(t / c * 1e3, 2), "launches": c} for n, (c, t) in prof.items()}
     step_bytes = kv_bytes + weight_bytes
-    # decode attention plus the norms: their kernels' summed event time per
+    # decode attention plus the norm kernels: their summed event time per
     # step against their algorithmic bytes (K/V once per group, q in, attention
-    # out; the norms read x (bf16) and h (fp32) and write the bf16 operands)
+    # out; norm 1 reads x (bf16) and writes its operand; a separate norm 2
+    # reads h (fp32) and writes its operand -- at decode sizes that norm runs
+    # inside the o_proj GEMM's split-K pass and is not counted here)
     T = w.batch
     an_kernels = [k for k in ("attn_decode_split", "attn_decode_combine", "rms_rowscale", "rms_convert")
                   if k in prof]
     an_us = sum(prof[k][1] / prof[k][0] * 1e3 for k in an_kernels)
-    an_bytes = (kv_bytes_prof + 2 * T * H * D * 2            # K/V, q, attention output
-                + T * d * 2 * 2 + T * d * 4 + T * d * 2)     # norm 1 (x in, operand out), norm 2 (h in, operand out)
+    an_bytes = (kv_bytes_prof + 2 * T * H * D * 2                      # K/V, q, attention output
+                + (T * d * 2 * 2 if "rms_rowscale" in prof else 0)     # norm 1
+                + (T * d * 4 + T * d * 2 if "rms_convert" in prof else 0))  # norm 2
     an_ach = an_bytes / (an_us * 1e-6) / 1e9
     log(f"[bench] decode {us:.1f} us/step ({us_prof:.1f} with per-kernel events), "
         f"{step_bytes / (us * 1e-6) / 1e9:.0f} GB/s whole step")

@@ -400,9 +400,14 @@ __global__ __launch_bounds__(256, NG == 1 ? 3 : 2) void attn_decode_wave_kernel(
       float p[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) p[e] = fast_exp2(sc[e] - m_new);
-      l_run[ng] = l_run[ng] * alpha + (p[0] + p[1]) + (p[2] + p[3]);
-      m_run[ng] = m_new;
+      // P in bf16 (the O^T product's operand); the row sum adds the same
+      // bf16 values, so O / l is a weighted mean of V with weights summing to one
       const bf16x4 pb = {from_f32<bf16>(p[0]), from_f32<bf16>(p[1]), from_f32<bf16>(p[2]), from_f32<bf16>(p[3])};
+      const bf16x2 ones2 = {from_f32<bf16>(1.f), from_f32<bf16>(1.f)};
+      float ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[0], pb[1]}, ones2, 0.f, false);
+      ps = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[2], pb[3]}, ones2, ps, false);
+      l_run[ng] = l_run[ng] * alpha + ps;
+      m_run[ng] = m_new;
       const u32x2 pw = __builtin_bit_cast(u32x2, pb);
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) o[ng][db] = mfma16x16x16(o[ng][db] * alpha, r.v[db], pw);

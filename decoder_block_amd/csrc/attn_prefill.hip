@@ -30,6 +30,8 @@
 // the DMAs took about 40% of the kernel's time on top of the math.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -413,9 +415,13 @@ __global__ __launch_bounds__(512) void attn_prefill_f32_kernel(const T* __restri
 //    keeps the fragment reads free of bank conflicts.
 //  * LDS fragment addresses are per-lane bases computed once plus the slot
 //    offset.
-//  * q arrives scaled by log2(e)/sqrt(D), and the QK product starts from an
-//    accumulator holding -m (the row's running max), so the MFMA result is
-//    already s - m in exp2 units: p = exp2(acc) with no VALU step between.
+//  * q arrives scaled by log2(e)/sqrt(D), so scores come out in exp2 units.
+//  * The online softmax runs per 64-key tile: both 32-key halves' S^T
+//    products, one max and rescale decision per tile, then the second half's
+//    exponentials overlap the first half's O^T product in the matrix core.
+//    The causal mask is applied only on the tiles that reach a row's
+//    diagonal (a separate copy of the tile loop).  P is rounded to
+//    bf16 for the O^T product and the row sum adds those same bf16 values.
 // ---------------------------------------------------------------------------
 template <int D>
 struct BCfg {
@@ -571,9 +577,7 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
 
   float m_run = 0.f, l_run = 0.f;  // m_run: running max in exp2 units (valid once `first` is false)
   bool first = true;
-  f32x16 negm, o[C::NDB];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) negm[i] = 0.f;
+  f32x16 o[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
 #pragma unroll
@@ -590,88 +594,176 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
   finish(0, 0);
   __syncthreads();
 
+  // One 64-key tile of the online softmax.  Both 32-key halves' S^T products
+  // are issued back to back; the running max is checked once per tile; then
+  // the exponentials of the second half run while the first half's O^T
+  // product is in the matrix core.  The whole tile is one straight-line block
+  // apart from the rare rescale, so the compiler can interleave one half's
+  // VALU work with the other half's MFMAs.  Only tiles that reach a row's
+  // diagonal (DIAG) apply the causal mask.
   const char* lds = reinterpret_cast<const char*>(ring);
-  for (int kt = 0; kt < ntiles; ++kt) {
+  const bf16x2 ones2 = {from_f32<bf16>(1.f), from_f32<bf16>(1.f)};
+  auto tile = [&](const char* sb, int k0, auto diag_) {
+    constexpr bool DIAG = decltype(diag_)::value;
+    auto kfrag = [&](int kb, int kk) {
+      return *reinterpret_cast<const bf16x8*>(sb + kaddr[kk] + kb * 32 * C::CPRK * 16);
+    };
+    auto vfrag = [&](int kb, int m, int db) {
+      return *reinterpret_cast<const bf16x8*>(sb + vaddr + (2 * kb + m) * C::PIECE + db * 32 * 32);
+    };
+    auto start = [&](int) {  // the accumulator S^T starts from
+      f32x16 init;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) init[i] = 0.f;
+      return init;
+    };
+    // causal mask on tiles that reach a row's diagonal: scores of keys after
+    // the row's position are replaced (not added to: the K rows of positions
+    // past the sequence's end hold whatever the pool held, possibly NaN bits)
+    auto mask = [&](f32x16& sc, int kb) {
+      if constexpr (DIAG) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kp = k0 + 32 * kb + 8 * (i >> 2) + 4 * hl + (i & 3);
+          if (kp > qpos) sc[i] = -INFINITY;
+        }
+      }
+    };
+    // stage 1: K fragments of the first half
+    bf16x8 ka[C::NQ], kb1[C::NQ];
+#pragma unroll
+    for (int kk = 0; kk < C::NQ; ++kk) ka[kk] = kfrag(0, kk);
+    __builtin_amdgcn_sched_barrier(0);
+    // stage 2: S^T of the first half || K fragments of the second half
+    f32x16 sc0 = mfma32_chunk(start(0), ka[0], qf[0]);
+#pragma unroll
+    for (int kk = 1; kk < C::NQ; ++kk) sc0 = mfma32_chunk(sc0, ka[kk], qf[kk]);
+#pragma unroll
+    for (int kk = 0; kk < C::NQ; ++kk) kb1[kk] = kfrag(1, kk);
+#pragma unroll
+    for (int kk = 0; kk < C::NQ; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // stage 3: S^T of the second half || max of the first half
+    // (scores are in exp2 units: q arrives scaled by log2(e)/sqrt(D))
+    f32x16 sc1 = mfma32_chunk(start(1), kb1[0], qf[0]);
+#pragma unroll
+    for (int kk = 1; kk < C::NQ; ++kk) sc1 = mfma32_chunk(sc1, kb1[kk], qf[kk]);
+    mask(sc0, 0);
+    float mx = sc0[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc0[i]);
+#pragma unroll
+    for (int kk = 0; kk < C::NQ; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // stage 4: V^T fragments of the first half (their latency hides behind
+    // the rest of the softmax), then the online softmax: lane = one query row,
+    // 32 of the tile's 64 keys
+    bf16x8 va0[2][C::NDB];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) va0[m][db] = vfrag(0, m, db);
+    mask(sc1, 1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc1[i]);
+    {  // max with lane l ^ 32 (the row's other 32 keys)
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
+                                                       __builtin_bit_cast(unsigned, mx), false, false);
+      mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
+    }
+    // the running max m is raised lazily: only when a score exceeds it by
+    // more than 2^8, so unnormalised P stays <= 256; the final division uses
+    // the same stale max, so the result is exact
+    const bool grow = first || mx - m_run > kRescaleLog2;
+    if (wave_any(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = first ? 0.f : fast_exp2(m_run - m_new);
+      m_run = m_new;
+      first = false;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
+    }
+    // P in bf16 (the O^T product's operand); the row sum adds the same bf16
+    // values, so O / l is a weighted mean of V with weights summing to one
+    bf16x8 p0[2], p1[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p0[i >> 3][i & 7] = from_f32<bf16>(fast_exp2(sc0[i] - m_run));
+    __builtin_amdgcn_sched_barrier(0);
+    // stage 5: O^T += V^T P^T for the first half || exponentials of the second
+    // half, V^T fragments of the second half
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) o[db] = mfma32_chunk(o[db], va0[m][db], p0[m]);
+    bf16x8 va1[2][C::NDB];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) va1[m][db] = vfrag(1, m, db);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p1[i >> 3][i & 7] = from_f32<bf16>(fast_exp2(sc1[i] - m_run));
+#pragma unroll
+    for (int kk = 0; kk < 2 * C::NDB; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // stage 6: O^T += V^T P^T for the second half || row sums
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) o[db] = mfma32_chunk(o[db], va1[m][db], p1[m]);
+    float psum = 0.f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p0[m][2 * e], p0[m][2 * e + 1]}, ones2, psum, false);
+        psum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{p1[m][2 * e], p1[m][2 * e + 1]}, ones2, psum, false);
+      }
+    l_run += psum;
+#pragma unroll
+    for (int kk = 0; kk < 2 * C::NDB; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // One iteration of the tile loop: the next DMA into the freed slot, the
+  // tile (skipped when it is past every row of this wave), then the wait for
+  // the next tile and the barrier that publishes it.
+  auto step = [&](int kt, auto diag) {
     const int st = kt % C::NST;
     const int k0 = kt * C::KT;
     if (kt + C::NST - 1 < ntiles) {
       issue((kt + C::NST - 1) % C::NST, bk_next);
       bk_next = block_of(min(kt + C::NST, ntiles - 1));
     }
-    const char* sb = lds + st * C::SLOT;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kh = k0 + 32 * kb;
-      if (kh > wmax) continue;  // every row of this wave is before these keys
-      // ---- S^T - m = K Q^T + (-m) ----
-      bf16x8 ka[C::NQ];
-#pragma unroll
-      for (int kk = 0; kk < C::NQ; ++kk)
-        ka[kk] = *reinterpret_cast<const bf16x8*>(sb + kaddr[kk] + kb * 32 * C::CPRK * 16);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 sc = mfma32_chunk(negm, ka[0], qf[0]);
-#pragma unroll
-      for (int kk = 1; kk < C::NQ; ++kk) sc = mfma32_chunk(sc, ka[kk], qf[kk]);
-      // V^T fragments of the half: their latency hides behind the softmax
-      bf16x8 va[2][C::NDB];
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          va[m][db] = *reinterpret_cast<const bf16x8*>(sb + vaddr + (2 * kb + m) * C::PIECE + db * 32 * 32);
-        }
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- online softmax: lane = one query row, 16 of the half's 32 keys ----
-      if (kh + 31 > wmin) {  // the half reaches the diagonal of some row of this wave
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kp = kh + 8 * (i >> 2) + 4 * hl + (i & 3);
-          if (kp > qpos) sc[i] = -INFINITY;
-        }
-      }
-      float mx = sc[0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sc[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));  // max of s - m over the 32 keys
-      // the running max is raised lazily: only when a score exceeds it by
-      // more than 2^8, so unnormalised P stays <= 256; the final division
-      // uses the same stale max, so the result is exact
-      const bool grow = first || mx > kRescaleLog2;
-      if (wave_any(grow)) {
-        const float shift = grow ? mx : 0.f;
-        const float alpha = first ? 0.f : fast_exp2(-shift);
-        m_run = first ? mx : m_run + shift;
-        first = false;
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sc[i] -= shift;
-          negm[i] = -m_run;
-        }
-      }
-      bf16x8 pv[2];
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(sc[i]);
-        psum += p;
-        pv[i >> 3][i & 7] = from_f32<bf16>(p);
-      }
-      l_run += psum;
-      // ---- O^T += V^T P^T ----
-#pragma unroll
-      for (int m = 0; m < 2; ++m)
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) o[db] = mfma32_chunk(o[db], va[m][db], pv[m]);
-    }
+    if (k0 <= wmax) tile(lds + st * C::SLOT, k0, diag);
     if (kt + 1 < ntiles) {
       wait_tile(kt + 1);
       finish(kt + 1, (kt + 1) % C::NST);
     }
     __syncthreads();
-  }
+  };
+  // Tiles up to the first one holding a key after some row of this wave need
+  // no mask; from there on every tile takes the masked path (keys past the
+  // sequence's end are after every row, so the last tile is always masked).
+  // Two loops rather than a branch per tile: each holds one copy of the tile,
+  // which keeps the register allocation of each free of the other.
+  const int kt_diag = min(ntiles, wmin >= C::KT - 1 ? (wmin - (C::KT - 1)) / C::KT + 1 : 0);
+  int kt = 0;
+  for (; kt < kt_diag; ++kt) step(kt, std::false_type{});
+  for (; kt < ntiles; ++kt) step(kt, std::true_type{});
 
   if (!active) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -693,6 +785,7 @@ template <typename T, int D>
 hipError_t launch_d(const void* q, void* attn, int H, const CacheView& c, const BatchView& b, hipStream_t s) {
   const int R = H / c.G;
   const int P = ACfg<T, D>::ROWS / R;
+  static_assert(ACfg<T, D>::ROWS == BCfg<D>::ROWS, "same rows per workgroup");
   dim3 grid(c.G * b.batch, (b.seq_len + P - 1) / P);
   if constexpr (sizeof(T) == 2)
     attn_prefill_bf16_kernel<D><<<grid, BCfg<D>::NT, 0, s>>>(reinterpret_cast<const bf16*>(q),

@@ -114,11 +114,21 @@ DEVI void store_head4(T* head, int dd, f32x4 v, int half_split, int D) {
   }
 }
 
+// RMSNorm row scale of token t: precomputed, or from the per-segment sums of
+// squares that a folded norm pass left (added in segment order).
+DEVI float row_scale(const GemmArgs& a, int t) {
+  if (a.ss_part == nullptr) return a.rowscale[t];
+  const float* p = a.ss_part + (size_t)t * a.ss_nseg;
+  float acc = 0.f;
+  for (int i = 0; i < a.ss_nseg; ++i) acc += p[i];
+  return 1.f / sqrtf(acc / (float)a.ss_d + a.eps);
+}
+
 // Epilogue for one lane-quad: token t, features f .. f+3, accumulator v.
 template <typename T, int EPI>
 DEVI void epilogue(const GemmArgs& a, int t, int f, f32x4 v) {
   if constexpr (EPI == (int)Epi::QKV) {
-    const float r = a.rowscale[t];
+    const float r = row_scale(a, t);
     v *= r;
     const int D = a.cache.D, G = a.cache.G;
     const int HD = a.H * D, KD = G * D;
@@ -159,7 +169,7 @@ DEVI void epilogue(const GemmArgs& a, int t, int f, f32x4 v) {
     f32x4 x = load4(reinterpret_cast<const T*>(a.resid) + o);
     *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = x + v;
   } else if constexpr (EPI == (int)Epi::SWIGLU) {
-    const float r = a.rowscale[t];
+    const float r = row_scale(a, t);
     v *= r;
     const float s0 = silu(v[0]) * v[1];
     const float s1 = silu(v[2]) * v[3];
@@ -331,44 +341,54 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Large bf16 tiles: 256 features x 256 tokens, four waves (one per SIMD), each
-// wave 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16 whose
-// accumulators (256 registers) stay in the matrix core's register file.
-// A stage is 8 CPR elements of K (CPR / 2 k-steps of 16) held in one slot of
-// an NS-slot LDS ring (in use: CPR 4, NS 4, i.e. 32-element stages in 4
-// slots).  Each k-step is 8 slices of two MFMAs plus one LDS read of the next
-// k-step's fragments (read in the order the MFMAs consume them), so with a
-// single wave per SIMD the matrix core does not wait for LDS:
+// Large bf16 tiles: 256 features x BM tokens (BM 256 or 128), four waves (one
+// per SIMD) as 2 x 2, each wave 128 features x BM/2 tokens as 4 x BM/64
+// blocks of v_mfma_f32_32x32x16_bf16 whose accumulators stay in the matrix
+// core's register file.  BM 128 is for launches that 256 x 256 tiles would
+// give fewer than two rounds of the 256 CUs (e.g. the 4096-feature
+// projections of a 2048-token prefill: 128 tiles).
+// K is staged 32 elements at a time (two k-steps of 16) in a 4-slot LDS
+// ring.  Each k-step is BM/32 slices of two MFMAs plus LDS reads of the next
+// k-step's fragments (in the order the MFMAs consume them), so with a single
+// wave per SIMD the matrix core does not wait for LDS:
 //   k-step 0 of stage kt: MFMAs || reads of k-step 1;
 //   wait for this wave's DMAs of stage kt+1, barrier (every wave is done
 //   with stage kt-1);
 //   last k-step: MFMAs || reads of k-step 0 of stage kt+1 || DMAs of stage
-//   kt+NS-1 into stage kt-1's slot, spread over the slices.
-// Waves 0-1 move the W rows of a stage and waves 2-3 the X rows.
+//   kt+3 into stage kt-1's slot, spread over the slices.
 // 32x32 result layout: lane l holds token (l & 31) and, in registers
 // 4g..4g+3, features 8g + 4(l >> 5) + {0..3}: four lane-local groups of four
 // consecutive features, so the same epilogues apply.
 // ---------------------------------------------------------------------------
-template <int CPR_, int NS_>
+template <int BM_>
 struct BigCfg {
-  static constexpr int BN = 256, BM = 256, NT = 256, CPR = CPR_, NS = NS_, KS = CPR / 2, BK = 8 * CPR;
+  static constexpr int BN = 256, BM = BM_, NT = 256, CPR = 4, NS = 4, KS = 2, BK = 32;
+  static constexpr int TW = BM / 2;                 // tokens per wave
+  static constexpr int TJ = TW / 32;                // 32-token MFMA blocks per wave
+  static constexpr int NF = 4 + TJ;                 // fragments per k-step: 4 of W, TJ of X
+  static constexpr int NSL = 2 * TJ;                // slices of two MFMAs per k-step
   static constexpr int PER = (BN + BM) * CPR / NT;  // DMAs per thread per stage
   static constexpr int SLOT = (BN + BM) * CPR;      // 16-byte chunks per slot
-  static_assert(CPR == 4 || CPR == 8, "32 or 64 K-elements per stage");
-  static_assert(PER % 8 == 0, "DMAs spread evenly over the 8 slices of a k-step");
+  static constexpr int HALVES = BM / 128;           // 128-token passes of the staged epilogues
+  // LDS: the ring, which the epilogues reuse to stage 128 tokens x 256 fp32
+  // features (128 KB) at a time
+  static constexpr int LDS_CHUNKS = NS * SLOT > 128 * 64 ? NS * SLOT : 128 * 64;
+  static_assert(BM == 256 || BM == 128, "256 or 128 tokens per tile");
   // 16 consecutive rows read one chunk each: the XOR spreads them over all
   // 16-byte positions of a 256-byte bank window
-  static DEVI int swz(int r, int c) {
-    if constexpr (CPR == 4) return r * 4 + (c ^ ((r >> 2) & 3));
-    else return r * 8 + (c ^ ((r >> 1) & 7));
-  }
+  static DEVI int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+  // the staged epilogues handle 128 tokens at a time: wave row wm writes its
+  // accumulators in pass hh when its tokens fall in that pass
+  static DEVI bool in_pass(int wm, int hh) { return (wm * TW) / 128 == hh; }
+  static DEVI int pass_row(int wm, int hh) { return wm * TW - hh * 128; }
 };
 
-template <int EPI, int CPR, int NS>
+template <int EPI, int BM>
 __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
-  using C = BigCfg<CPR, NS>;
+  using C = BigCfg<BM>;
+  constexpr int NS = C::NS, TJ = C::TJ, NF = C::NF, NSL = C::NSL;
   using T = bf16;
-  __shared__ u32x4 ring[NS * C::SLOT];
+  __shared__ u32x4 ring[C::LDS_CHUNKS];
 
   const int tiles_n = a.N / C::BN;
   const int tiles_m = (a.M + C::BM - 1) / C::BM;
@@ -389,9 +409,10 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
   const int wn = wave & 1, wm = wave >> 1;
 
   // The tile's stage kt is one 16 KB piece of 64-byte rows for W (K-block-major,
-  // stages w_rows * 64 bytes apart) and one for X (256 x 32 tiles, 16 KB apart),
-  // so every DMA fetches whole cache lines.  A lane's 16 bytes sit at the same
-  // offset inside every stage.
+  // stages w_rows * 64 bytes apart) and a 16 KB (BM 256) or 8 KB (BM 128, half
+  // of a 256-row tile) piece for X (256 x 32 tiles, 16 KB apart), so every DMA
+  // fetches whole cache lines.  A lane's 16 bytes sit at the same offset inside
+  // every stage.
   static_assert(C::BK == kTileCols, "one tile column block per stage");
   constexpr int STAGE_BYTES = kTileElems * 2;
   int voff[C::PER];
@@ -415,44 +436,45 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
   };
   auto rsrc_x = [&](int kt) {
     const bool live = kt < nk;
-    return make_rsrc(Xt + (live ? kt * STAGE_BYTES : 0), live ? (uint32_t)STAGE_BYTES : 0u);
+    return make_rsrc(Xt + (live ? kt * STAGE_BYTES : 0), live ? (uint32_t)(C::BM * 64) : 0u);
   };
   auto dma = [&](int i, const i32x4& rW, const i32x4& rX, uint32_t slot_base) {
     const int q = wave * C::PER + i;  // DMA group: W rows while q * 64 < BN * CPR
     buf_dma16_to(q * 64 < C::BN * C::CPR ? rW : rX, slot_base + (uint32_t)(q * 1024), voff[i]);
   };
 
-  f32x16 acc[4][4];
+  f32x16 acc[4][TJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int l32 = lane & 31, lh = lane >> 5;
-  bf16x8 fr0[8], fr1[8];
-  // fragment r of k-step ks, in the order the MFMAs first use them:
-  // A0, B0, B1, B2, B3, A1, A2, A3 (MFMAs run (i, j) i-major)
-  auto frag_addr = [&](int r, int ks) {
+  bf16x8 fr0[NF], fr1[NF];
+  // fragment f of k-step ks, in the order the MFMAs first use them:
+  // A0, B0 .. B(TJ-1), A1, A2, A3 (MFMAs run (i, j) i-major)
+  auto frag_addr = [&](int f, int ks) {
     const int c = 2 * ks + lh;
-    if (r == 0) return C::swz(wn * 128 + l32, c);
-    if (r <= 4) return C::swz(C::BN + wm * 128 + 32 * (r - 1) + l32, c);
-    return C::swz(wn * 128 + 32 * (r - 4) + l32, c);
+    if (f == 0) return C::swz(wn * 128 + l32, c);
+    if (f <= TJ) return C::swz(C::BN + wm * C::TW + 32 * (f - 1) + l32, c);
+    return C::swz(wn * 128 + 32 * (f - TJ) + l32, c);
   };
-  auto fa = [](bf16x8 (&f)[8], int i) -> bf16x8& { return i == 0 ? f[0] : f[4 + i]; };
-  auto fb = [](bf16x8 (&f)[8], int j) -> bf16x8& { return f[1 + j]; };
-  auto kstep = [&](bf16x8 (&cur)[8], bf16x8 (&nxt)[8], const u32x4* L, int nks, bool with_dma, const i32x4& rW,
+  auto fa = [](bf16x8 (&f)[NF], int i) -> bf16x8& { return i == 0 ? f[0] : f[TJ + i]; };
+  auto fb = [](bf16x8 (&f)[NF], int j) -> bf16x8& { return f[1 + j]; };
+  auto kstep = [&](bf16x8 (&cur)[NF], bf16x8 (&nxt)[NF], const u32x4* L, int nks, bool with_dma, const i32x4& rW,
                    const i32x4& rX, uint32_t dma_base) {
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int i = r >> 1, j0 = 2 * (r & 1);
+    for (int r = 0; r < NSL; ++r) {
+      const int i = r / (TJ / 2), j0 = 2 * (r % (TJ / 2));
       acc[i][j0] = mfma32_chunk(acc[i][j0], fa(cur, i), fb(cur, j0));
       acc[i][j0 + 1] = mfma32_chunk(acc[i][j0 + 1], fa(cur, i), fb(cur, j0 + 1));
-      nxt[r] = __builtin_bit_cast(bf16x8, L[frag_addr(r, nks)]);
+#pragma unroll
+      for (int f = r; f < NF; f += NSL) nxt[f] = __builtin_bit_cast(bf16x8, L[frag_addr(f, nks)]);
       if (with_dma) {
 #pragma unroll
-        for (int u = 0; u < C::PER / 8; ++u) dma(r * (C::PER / 8) + u, rW, rX, dma_base);
+        for (int u = r; u < C::PER; u += NSL) dma(u, rW, rX, dma_base);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -487,25 +509,22 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
   wait_vmcnt<(NS - 2) * C::PER>();
   lds_barrier();
 #pragma unroll
-  for (int r = 0; r < 8; ++r) fr0[r] = __builtin_bit_cast(bf16x8, ring[frag_addr(r, 0)]);
+  for (int f = 0; f < NF; ++f) fr0[f] = __builtin_bit_cast(bf16x8, ring[frag_addr(f, 0)]);
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
   int kt = 0;
-  if constexpr (NS == 4) {
-    for (; kt + 4 <= nk; kt += 4) {
-      stage(kt, I0{});
-      stage(kt + 1, I1{});
-      stage(kt + 2, I2{});
-      stage(kt + 3, I3{});
-    }
-    if (kt < nk) {  // nk is even: at most two stages remain (slots 0, 1)
-      stage(kt, I0{});
-      stage(kt + 1, I1{});
-    }
-  } else {
-    static_assert(NS == 4, "ring of four slots");
+  static_assert(NS == 4, "ring of four slots");
+  for (; kt + 4 <= nk; kt += 4) {
+    stage(kt, I0{});
+    stage(kt + 1, I1{});
+    stage(kt + 2, I2{});
+    stage(kt + 3, I3{});
+  }
+  if (kt < nk) {  // nk is even: at most two stages remain (slots 0, 1)
+    stage(kt, I0{});
+    stage(kt + 1, I1{});
   }
   wait_vmcnt<0>();
 
@@ -519,8 +538,8 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
     bf16* st = reinterpret_cast<bf16*>(ring);
     __syncthreads();  // every wave is done with the ring
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tl = wm * 128 + 32 * j + l32;
+    for (int j = 0; j < TJ; ++j) {
+      const int tl = wm * C::TW + 32 * j + l32;
       const float r = m0 + tl < a.M ? a.rowscale[m0 + tl] : 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -529,19 +548,21 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
           const int cl = wn * 64 + 16 * i + 4 * g + 2 * lh;  // s column inside the tile (even)
           const float v0 = acc[i][j][4 * g] * r, v1 = acc[i][j][4 * g + 1] * r;
           const float v2 = acc[i][j][4 * g + 2] * r, v3 = acc[i][j][4 * g + 3] * r;
-          *reinterpret_cast<bf16x2*>(st + ((cl >> 5) * 256 + tl) * RS + (cl & 31)) =
+          *reinterpret_cast<bf16x2*>(st + ((cl >> 5) * C::BM + tl) * RS + (cl & 31)) =
               bf16x2{from_f32<bf16>(silu(v0) * v1), from_f32<bf16>(silu(v2) * v3)};
         }
     }
     __syncthreads();
+    // m0 may be the second half of a 256-row tile (BM 128): tiled_off places
+    // the tile's first row, and rows of one column block are 64 bytes apart
     bf16* ob = reinterpret_cast<bf16*>(a.out) + tiled_off(m0, n0 / 2, a.ldo);
 #pragma unroll
-    for (int p = 0; p < 16; ++p) {
+    for (int p = 0; p < C::BM / 16; ++p) {
       const int idx = p * 256 + tid;  // 16-byte piece: column block, row, chunk
-      const int cb = idx >> 10, row = (idx >> 2) & 255, ch = idx & 3;
+      const int cb = idx / (C::BM * 4), row = (idx >> 2) % C::BM, ch = idx & 3;
       if (m0 + row < a.M)
         *reinterpret_cast<u32x4*>(ob + cb * kTileElems + row * 32 + ch * 8) =
-            *reinterpret_cast<const u32x4*>(st + (cb * 256 + row) * RS + ch * 8);
+            *reinterpret_cast<const u32x4*>(st + (cb * C::BM + row) * RS + ch * 8);
     }
     return;
   }
@@ -562,15 +583,15 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
     const float qs = q_scale(D);
     __syncthreads();  // every wave is done with the ring
 #pragma unroll 1
-    for (int hh = 0; hh < 2; ++hh) {
-      if (wm == hh) {
+    for (int hh = 0; hh < C::HALVES; ++hh) {
+      if (C::in_pass(wm, hh)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const int r = 32 * j + l32, c = (wn * 128 + 32 * i + 8 * g + 4 * lh) >> 2;
+              const int r = C::pass_row(wm, hh) + 32 * j + l32, c = (wn * 128 + 32 * i + 8 * g + 4 * lh) >> 2;
               st[r * 64 + (c ^ (r & 63))] =
                   f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
             }
@@ -672,7 +693,7 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
     f32x4* st = reinterpret_cast<f32x4*>(ring);
     __syncthreads();  // every wave is done with the ring
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
+    for (int hh = 0; hh < C::HALVES; ++hh) {
       // the half's residual rows are loaded first, so that their latency
       // overlaps the LDS writes and the barrier
       f32x4 res[32];
@@ -685,14 +706,14 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
         else
           res[p] = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(a.resid) + o);
       }
-      if (wm == hh) {
+      if (C::in_pass(wm, hh)) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const int r = 32 * j + l32, c = (wn * 128 + 32 * i + 8 * g + 4 * lh) >> 2;
+              const int r = C::pass_row(wm, hh) + 32 * j + l32, c = (wn * 128 + 32 * i + 8 * g + 4 * lh) >> 2;
               st[r * 64 + (c ^ (r & 63))] =
                   f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
             }
@@ -724,8 +745,8 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = m0 + wm * 128 + 32 * j + l32;
+    for (int j = 0; j < TJ; ++j) {
+      const int t = m0 + wm * C::TW + 32 * j + l32;
       if (t < a.M) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -768,12 +789,44 @@ __global__ __launch_bounds__(256) void gemm_split_reduce_kernel(GemmArgs a, int 
   epilogue<bf16, EPI>(a, t, f, v);
 }
 
+// RESID_H pass that also runs the second RMSNorm (bf16): workgroup (segment,
+// token) adds the K partials of 1024 features in slice order, writes
+// h = x + sum, h * gamma_2 rounded to bf16 in the gate/up GEMM's tiled order,
+// and the segment's sum of h^2 (lanes, then waves, in a fixed order); the
+// gate/up epilogue adds the row's segments in order, so the result does not
+// depend on timing.
+__global__ __launch_bounds__(256) void gemm_split_reduce_norm_kernel(GemmArgs a, int KS) {
+  const int seg = blockIdx.x, t = blockIdx.y;
+  const int f = seg * kNormSeg + threadIdx.x * 4;
+  float ss = 0.f;
+  if (f < a.N) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(a.split_ws + (size_t)t * a.N + f);
+    const size_t slice = (size_t)a.M * a.N / 4;
+    f32x4 v = p[0];
+    for (int k = 1; k < KS; ++k) v += p[k * slice];
+    const size_t o = (size_t)t * a.ldo + f;
+    const f32x4 h = load4(reinterpret_cast<const bf16*>(a.resid) + o) + v;
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = h;
+    ss = h[0] * h[0] + h[1] * h[1] + h[2] * h[2] + h[3] * h[3];
+    const f32x4 g = h * *reinterpret_cast<const f32x4*>(a.norm_gamma + f);
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(a.norm_out) + tiled_off(t, f, a.N)) =
+        bf16x4{from_f32<bf16>(g[0]), from_f32<bf16>(g[1]), from_f32<bf16>(g[2]), from_f32<bf16>(g[3])};
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) ss += shfl_xor(ss, m);
+  __shared__ float wsum[4];
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0) a.ss_part[(size_t)t * a.ss_nseg + seg] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
 // ---------------------------------------------------------------------------
 // Weight-streaming bf16 GEMM for few tokens, staged through LDS.  A workgroup
 // owns 64 features x 64 tokens and one of KS slices of K.  Stages of 64
 // K-elements (W: 64 rows x 128 B, X: 64 rows x 128 B) are moved by LDS DMA
 // into a ring of NSL slots, NSL - 1 stages ahead (8 slots and one workgroup
-// per CU measured 3-8% slower on the 8B shapes), each DMA instruction
+// per CU measured 2-7% slower on the 8B decode shapes, also for launches of
+// at most one workgroup per CU), each DMA instruction
 // fetching whole 128-byte row segments.  Wave w computes features 16w..16w+15
 // for all 64 tokens, so no cross-wave reduction is needed.
 // ---------------------------------------------------------------------------
@@ -874,7 +927,9 @@ template <int EPI>
 hipError_t launch_skinny_epi(const GemmArgs& a, int KS, hipStream_t s) {
   dim3 grid(a.N / 64, (a.M + 63) / 64, KS);
   gemm_stream_kernel<EPI><<<grid, 256, 0, s>>>(a, KS);
-  if (KS > 1) {
+  if (EPI == 1 && a.norm_gamma) {
+    gemm_split_reduce_norm_kernel<<<dim3(a.ss_nseg, a.M), 256, 0, s>>>(a, KS);
+  } else if (KS > 1) {
     const size_t n = (size_t)a.M * (a.N / 4);
     gemm_split_reduce_kernel<EPI><<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a, KS);
   }
@@ -885,6 +940,10 @@ hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
   if (a.N % 64 != 0 || a.K % 64 != 0 || a.M <= 0 || a.M > 256) return hipErrorInvalidValue;
   const int KS = skinny_ks(a.M, a.N, a.K);
   if (KS > 1 && (a.split_ws == nullptr || a.split_ws_bytes < (size_t)KS * a.M * a.N * sizeof(float)))
+    return hipErrorInvalidValue;
+  // the folded norm needs the split pass and whole 1024-feature segments
+  if (a.norm_gamma && (a.epi != Epi::RESID_H || KS == 1 || !a.norm_out || !a.ss_part ||
+                       a.ss_nseg != (a.N + kNormSeg - 1) / kNormSeg || a.ldo != a.N))
     return hipErrorInvalidValue;
   switch (a.epi) {
     case Epi::QKV: return launch_skinny_epi<0>(a, KS, s);
@@ -913,18 +972,30 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
-  constexpr int CPR = 4, NS = 4;
-  using C = BigCfg<CPR, NS>;
+template <int BM>
+hipError_t launch_big_bm(const GemmArgs& a, hipStream_t s) {
+  using C = BigCfg<BM>;
   if (a.N % C::BN != 0 || a.K % (2 * C::BK) != 0 || a.M <= 0) return hipErrorInvalidValue;
   const int grid = (a.N / C::BN) * ((a.M + C::BM - 1) / C::BM);
   switch (a.epi) {
-    case Epi::QKV: gemm_big_kernel<0, CPR, NS><<<grid, C::NT, 0, s>>>(a); break;
-    case Epi::RESID_H: gemm_big_kernel<1, CPR, NS><<<grid, C::NT, 0, s>>>(a); break;
-    case Epi::SWIGLU: gemm_big_kernel<2, CPR, NS><<<grid, C::NT, 0, s>>>(a); break;
-    case Epi::RESID_OUT: gemm_big_kernel<3, CPR, NS><<<grid, C::NT, 0, s>>>(a); break;
+    case Epi::QKV: gemm_big_kernel<0, BM><<<grid, C::NT, 0, s>>>(a); break;
+    case Epi::RESID_H: gemm_big_kernel<1, BM><<<grid, C::NT, 0, s>>>(a); break;
+    case Epi::SWIGLU: gemm_big_kernel<2, BM><<<grid, C::NT, 0, s>>>(a); break;
+    case Epi::RESID_OUT: gemm_big_kernel<3, BM><<<grid, C::NT, 0, s>>>(a); break;
   }
   return hipGetLastError();
+}
+
+// 256 x 256 tiles, or 256 x 128 when 256 x 256 would fill fewer than two
+// rounds of the 256 CUs (the half-height tile has two thirds of the
+// arithmetic intensity, so it pays only where it fills idle CUs)
+int big_tile_m(int M, int N) {
+  const long tiles256 = (long)(N / 256) * ((M + 255) / 256);
+  return tiles256 < 2 * 256 ? 128 : 256;
+}
+
+hipError_t launch_big(const GemmArgs& a, hipStream_t s) {
+  return big_tile_m(a.M, a.N) == 128 ? launch_big_bm<128>(a, s) : launch_big_bm<256>(a, s);
 }
 
 using SmallBF = Cfg<bf16, 64, 64, 2, 2>;

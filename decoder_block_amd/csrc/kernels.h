@@ -59,6 +59,16 @@ struct GemmArgs {
   // go here (skinny_partial_bytes) before one pass adds them and runs the epilogue
   float* split_ws;
   size_t split_ws_bytes;
+  // RMSNorm_2 folded into a split RESID_H pass (bf16 SKINNY, norm_gamma set):
+  // that pass also writes h * gamma as bf16 tiled [M][N] to norm_out and the
+  // row's sums of h^2 over 1024-feature segments to ss_part [M][ss_nseg]
+  const float* norm_gamma;
+  void* norm_out;
+  // QKV / SWIGLU: with ss_part set, the row scale is rsqrt(sum of the row's
+  // ss_nseg partial sums / ss_d + eps) instead of rowscale[t]
+  float* ss_part;
+  int ss_nseg, ss_d;
+  float eps;
 };
 
 // Tile shape chosen by the host for a GEMM.  SKINNY (bf16, M <= 128) is the
@@ -69,6 +79,8 @@ int gemm_tile_n(GemmTile t);  // features per workgroup tile
 // workgroups a SKINNY GEMM splits K into, and the partial-sum bytes it needs
 int skinny_ksplit(int M, int N, int K);
 size_t skinny_partial_bytes(int M, int N, int K);
+// feature segments of the folded RMSNorm_2 partial sums (one per 1024 features)
+constexpr int kNormSeg = 1024;
 
 hipError_t launch_gemm(DType t, GemmTile tile, const GemmArgs& a, hipStream_t s);
 

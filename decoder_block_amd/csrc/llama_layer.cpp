@@ -10,6 +10,8 @@
 //   attn = causal GQA attention(q, cache)             prefill: flash; decode: split-K
 //   h = x + attn Wo^T                                  fp32 residual stream
 //   r2 = rowscale(h), hb = h * gamma_2 in the layer dtype   RMSNorm_2
+//     (decode-sized calls: in the o_proj GEMM's split-K pass, with r2 finished
+//     in the gate/up epilogue from per-segment sums of h^2)
 //   s = SiLU(r2 * hb Wg^T) * (r2 * hb Wu^T)
 //   out = h + s Wd^T
 #include <hip/hip_runtime_api.h>
@@ -116,10 +118,17 @@ PackedLayout packed_layout(const Shape& s) {
 int max_splits_for(const Shape& s) { return (s.max_pos + llk::decode_split_keys() - 1) / llk::decode_split_keys(); }
 
 struct WsLayout {
-  size_t desc, r1, r2, xt, q, attn, h, hb, s, part, gpart, gpart_bytes, total;
+  size_t desc, r1, r2, ss, xt, q, attn, h, hb, s, part, gpart, gpart_bytes, total;
 };
 
 bool use_skinny(const Shape& sh, long M) { return sh.dt == DType::BF16 && M <= 128; }
+
+// RMSNorm_2 rides on the o_proj GEMM's split-K pass (no norm launch) when that
+// GEMM streams its weights with K split over workgroups.
+bool fold_norm2(const Shape& sh, long M) {
+  return use_skinny(sh, M) && llk::skinny_ksplit((int)M, sh.d, sh.HD) > 1;
+}
+int norm_segments(const Shape& sh) { return (sh.d + llk::kNormSeg - 1) / llk::kNormSeg; }
 
 // Split-K partial sums of the skinny GEMMs, for every token count up to T (the
 // size is non-decreasing in T, so a workspace sized for T serves every call
@@ -144,6 +153,8 @@ WsLayout ws_layout(const Shape& sh, size_t T, size_t B) {
   off = align256(off + T * sizeof(float));
   w.r2 = off;
   off = align256(off + T * sizeof(float));
+  w.ss = off;  // folded RMSNorm_2 partial sums (skinny calls only)
+  off = align256(off + (sh.dt == DType::BF16 ? std::min<size_t>(T, 128) * norm_segments(sh) * sizeof(float) : 0));
   const size_t Tp = op_rows(sh, T);  // GEMM operands: whole 256-row tiles (bf16)
   w.xt = off;
   off = align256(off + (sh.dt == DType::BF16 ? Tp * sh.d * sh.es : 0));
@@ -868,11 +879,20 @@ llama_status run_layer(llama_layer* L, const llk::CacheView& cv, const llk::Batc
   o.resid = x;
   o.out = h;
   o.ldo = s.d;
+  const float* gamma2 = reinterpret_cast<const float*>(P + L->pl.gamma2);
+  const bool fold2 = fold_norm2(s, M);
+  float* ss = reinterpret_cast<float*>(W + wl.ss);
+  if (fold2) {  // RMSNorm_2 statistics + operand copy in the split-K pass
+    o.norm_gamma = gamma2;
+    o.norm_out = hb;
+    o.ss_part = ss;
+    o.ss_nseg = norm_segments(s);
+  }
   HIP_TRY(timed(L, K_OPROJ, hs, [&] { return llk::launch_gemm(s.dt, tile_for(o.N), o, hs); }));
 
   // RMSNorm_2 statistics + operand copy
-  const float* gamma2 = reinterpret_cast<const float*>(P + L->pl.gamma2);
-  HIP_TRY(timed(L, K_RMS2, hs, [&] { return llk::launch_rms_convert(s.dt, h, gamma2, hb, r2, M, s.d, eps, hs); }));
+  if (!fold2)
+    HIP_TRY(timed(L, K_RMS2, hs, [&] { return llk::launch_rms_convert(s.dt, h, gamma2, hb, r2, M, s.d, eps, hs); }));
 
   // gate/up + SiLU * up
   llk::GemmArgs g{};
@@ -887,6 +907,12 @@ llama_status run_layer(llama_layer* L, const llk::CacheView& cv, const llk::Batc
   g.ldx = s.d;
   g.epi = llk::Epi::SWIGLU;
   g.rowscale = r2;
+  if (fold2) {
+    g.ss_part = ss;
+    g.ss_nseg = norm_segments(s);
+    g.ss_d = s.d;
+    g.eps = eps;
+  }
   g.out = sb;
   g.ldo = s.I_pad;
   HIP_TRY(timed(L, K_GATEUP, hs, [&] { return llk::launch_gemm(s.dt, tile_for(g.N), g, hs); }));

@@ -38,6 +38,7 @@ static std::string g_fail_launch;
 static void* g_scratch = nullptr;
 static int g_scratch_lookups = 0;
 static bool fails(const char* what) { return g_fail_launch == what; }
+static const float* g_ss_part = nullptr;  // partial sums the last folded norm wrote
 
 namespace llk {
 int gemm_tile_n(GemmTile t) { return t == GemmTile::LARGE ? 256 : 64; }
@@ -50,6 +51,16 @@ hipError_t launch_gemm(DType, GemmTile t, const GemmArgs& a, hipStream_t) {
   const char* tag = t == GemmTile::LARGE ? "L" : (t == GemmTile::SKINNY ? "K" : "S");
   g_log.push_back("gemm" + std::to_string((int)a.epi) + tag);
   if (fails(g_log.back().c_str())) return hipErrorLaunchFailure;
+  // RMSNorm_2 folded into the o_proj split pass: the operand copy and the
+  // partial sums come out of it, and the gate/up GEMM reads the same sums
+  if (a.norm_gamma) {
+    g_log.back() += "+norm2";
+    if (a.epi != Epi::RESID_H || !a.norm_out || !a.ss_part || a.ss_nseg != (a.N + kNormSeg - 1) / kNormSeg)
+      g_log.push_back("norm2-args-bad");
+    g_ss_part = a.ss_part;
+  }
+  if (a.epi == Epi::SWIGLU && a.ss_part != nullptr && (a.ss_part != g_ss_part || a.ss_d != a.K || !(a.eps > 0.f)))
+    g_log.push_back("norm2-sums-bad");
   if (a.epi == Epi::RESID_OUT) g_outs.push_back(a.out);
   if (t == GemmTile::SKINNY && a.split_ws_bytes < skinny_partial_bytes(a.M, a.N, a.K)) g_log.push_back("gemm-ws-short");
   return hipSuccess;
@@ -501,14 +512,16 @@ int main() {
     g_log.clear();
     CHECK(llama_layer_prefill(Lb, Cb, 2, 50, ids2, xb, ob, LLAMA_DTYPE_F32, wsb2, w1000, nullptr) == LLAMA_OK);
     {
-      const std::vector<std::string> want = {"rms1", "gemm0K", "attn_prefill", "gemm1K", "rms2", "gemm2K", "gemm3K"};
+      // split-K o_proj: RMSNorm_2 rides on its split pass
+      const std::vector<std::string> want = {"rms1", "gemm0K", "attn_prefill", "gemm1K+norm2", "gemm2K", "gemm3K"};
       CHECK(g_log == want);
     }
     g_log.clear();
     const int uploads_before = g_uploads;
     CHECK(llama_layer_decode(Lb, Cb, 2, ids2, xb, ob, LLAMA_DTYPE_BF16, wsb2, w1000, nullptr) == LLAMA_OK);
     CHECK(g_uploads == uploads_before);  // block table + descriptors ride on the first norm launch
-    CHECK(g_log.size() == 8 && g_log[1] == "gemm0K" && g_log[7] == "gemm3K");
+    CHECK(g_log.size() == 7 && g_log[1] == "gemm0K" && g_log[4] == "gemm1K+norm2" && g_log[5] == "gemm2K" &&
+          g_log[6] == "gemm3K");
     g_log.clear();
     CHECK(llama_layer_prefill(Lb, Cb, 1, 300, ids2, xb, ob, LLAMA_DTYPE_F32, wsb2, w1000, nullptr) == LLAMA_OK);
     {
