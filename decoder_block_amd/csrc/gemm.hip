@@ -83,12 +83,15 @@ DEVI f32x4 load4(const T* p) {
 
 // RoPE on two interleaved pairs (e, o) = (v0, v1), (v2, v3) at position pos,
 // pair index dd/2 and dd/2 + 1 of the head ("Chapter 10", section 3)
+DEVI f32x4 rotate4(f32x4 v, f32x2 cs, f32x2 sn) {
+  const float e0 = v[0], o0 = v[1], e1 = v[2], o1 = v[3];
+  return f32x4{e0 * cs[0] - o0 * sn[0], e0 * sn[0] + o0 * cs[0], e1 * cs[1] - o1 * sn[1], e1 * sn[1] + o1 * cs[1]};
+}
 DEVI f32x4 rope4(f32x4 v, const GemmArgs& a, int pos, int dd) {
   const int D = a.cache.D;
   const f32x2 cs = *reinterpret_cast<const f32x2*>(a.rope_cos + (size_t)pos * (D / 2) + dd / 2);
   const f32x2 sn = *reinterpret_cast<const f32x2*>(a.rope_sin + (size_t)pos * (D / 2) + dd / 2);
-  const float e0 = v[0], o0 = v[1], e1 = v[2], o1 = v[3];
-  return f32x4{e0 * cs[0] - o0 * sn[0], e0 * sn[0] + o0 * cs[0], e1 * cs[1] - o1 * sn[1], e1 * sn[1] + o1 * cs[1]};
+  return rotate4(v, cs, sn);
 }
 DEVI float q_scale(int D) { return 1.4426950408889634f * __frsqrt_rn((float)D); }
 
@@ -569,22 +572,32 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
 
   if constexpr (EPI == (int)Epi::QKV) {
     // QKV epilogue through LDS, one half of the tile (128 tokens, fp32) at a
-    // time (same layout as the residual epilogues below).  Pass 1 takes the q
-    // and k features a token row per wave instruction: row scale, RoPE with
-    // the cos/sin table rows read whole, q -> its [M][H*D] row, k -> its
-    // cache row.  Pass 2 takes the v features column-wise: the eight keys of a
-    // V^T cache row half (vperm_pos order) are gathered from LDS and stored as
-    // one 16-byte piece; blocks the half does not cover whole (ragged batch or
-    // sequence edges, continuation prefill) are stored key by key.
+    // time (same layout as the residual epilogues below), with the row scale
+    // r1 applied as the accumulators are staged.  Pass 1 takes the q and k
+    // features a token row per wave instruction: RoPE with the cos/sin table
+    // rows read whole, q -> its [M][H*D] row, k -> its cache row.  Pass 2 takes the v features column-wise: the
+    // eight keys of a V^T cache row half (vperm_pos order) are gathered from
+    // LDS and stored as one 16-byte piece, with the cache block of each
+    // 16-row group looked up once per half; blocks the half does not cover
+    // whole (ragged batch or sequence edges, continuation prefill) are stored
+    // key by key.
     f32x4* st = reinterpret_cast<f32x4*>(ring);
     float* stf = reinterpret_cast<float*>(ring);
+    __shared__ int vgrp[8];  // per 16-row group of the half: its cache block when whole, else -1
     const int D = a.cache.D, G = a.cache.G, HD = a.H * D, KD = G * D;
     const int S = a.batch.seq_len;
     const float qs = q_scale(D);
+    const bool has_v = n0 + C::BN > HD + KD && n0 < HD + 2 * KD;
     __syncthreads();  // every wave is done with the ring
 #pragma unroll 1
     for (int hh = 0; hh < C::HALVES; ++hh) {
       if (C::in_pass(wm, hh)) {
+        float rsj[TJ];
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) {
+          const int t = m0 + hh * 128 + C::pass_row(wm, hh) + 32 * j + l32;
+          rsj[j] = t < a.M ? a.rowscale[t] : 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -593,51 +606,75 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
             for (int g = 0; g < 4; ++g) {
               const int r = C::pass_row(wm, hh) + 32 * j + l32, c = (wn * 128 + 32 * i + 8 * g + 4 * lh) >> 2;
               st[r * 64 + (c ^ (r & 63))] =
-                  f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                  f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]} * rsj[j];
             }
+      }
+      if (has_v && tid < 8) {
+        const int t0 = m0 + hh * 128 + 16 * tid;
+        int blk = -1;
+        if (t0 + 15 < a.M) {
+          const int b0 = t0 / S;
+          const int pos0 = a.batch.desc[2 * b0 + 1] + (t0 - b0 * S);
+          if ((pos0 & 15) == 0 && (t0 + 15) / S == b0)
+            blk = a.cache.block_table[(size_t)a.batch.desc[2 * b0] * a.cache.max_blocks + (pos0 >> 4)];
+        }
+        vgrp[tid] = blk;
       }
       __syncthreads();
       // ---- pass 1: q and k ----
       const int f = n0 + 4 * lane;
       if (n0 < HD + KD) {
-        // per-row data of this wave's 32 rows (row 4p + wave), one row per
-        // lane, broadcast with readlane inside the loop
-        float rs_l = 0.f;
+        // token of row p of this wave: tb + 4p; per-row data one row per
+        // lane, broadcast with readlane
+        const int tb = m0 + hh * 128 + wave;
         int pos_l = 0, blk_l = 0;
         {
-          const int t = m0 + hh * 128 + 4 * (lane & 31) + wave;
+          const int t = tb + 4 * (lane & 31);
           if (t < a.M) {
             const int b = t / S;
             pos_l = a.batch.desc[2 * b + 1] + (t - b * S);
-            rs_l = a.rowscale[t];
             blk_l = a.cache.block_table[(size_t)a.batch.desc[2 * b] * a.cache.max_blocks + (pos_l >> 4)];
           }
         }
+        const bool qk = f < HD + KD;  // lanes past the k features hold v (pass 2)
         const int kf = f - HD, g = kf / D;
         const int dd = (f < HD ? f : kf) % D;
-#pragma unroll 8
-        for (int p = 0; p < 32; ++p) {
-          const int r = p * 4 + wave;
-          const int t = m0 + hh * 128 + r;
-          if (t >= a.M) break;  // rows grow with p
-          const float rs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rs_l), p));
-          const int pos = __builtin_amdgcn_readlane(pos_l, p);
-          if (f >= HD + KD) continue;
-          f32x4 v = st[r * 64 + (lane ^ (r & 63))] * rs;
-          v = rope4(v, a, pos, dd);
-          if (f < HD) {
-            v *= qs;
-            store_head4(reinterpret_cast<bf16*>(a.q_out) + (size_t)t * HD + (f - dd), dd, v, a.rope_half, D);
-          } else {
-            const size_t blk = (size_t)__builtin_amdgcn_readlane(blk_l, p);
-            store_head4(reinterpret_cast<bf16*>(a.cache.k_pool) + ((blk * G + g) * 16 + (pos & 15)) * D, dd, v,
-                        a.rope_half, D);
+        const float* cs_col = a.rope_cos + dd / 2;
+        const float* sn_col = a.rope_sin + dd / 2;
+        const int nrow = min(32, max(0, (a.M - tb + 3) >> 2));  // rows with t < M
+        // the RoPE table rows of 16 token rows are loaded before any of them is
+        // used (8, 16 and 32 rows measured within noise of each other; one
+        // row at a time, as a loop whose early exits sat before the loads,
+        // cost about 45 us per QKV launch at the LLaMA-3-8B shape and 8192 tokens)
+        constexpr int NB = 16;
+#pragma unroll 1
+        for (int p0 = 0; p0 < nrow; p0 += NB) {
+          f32x2 cs[NB], sn[NB];
+#pragma unroll
+          for (int u = 0; u < NB; ++u) {
+            const size_t o = (size_t)__builtin_amdgcn_readlane(pos_l, p0 + u) * (D / 2);
+            cs[u] = *reinterpret_cast<const f32x2*>(cs_col + o);
+            sn[u] = *reinterpret_cast<const f32x2*>(sn_col + o);
+          }
+#pragma unroll
+          for (int u = 0; u < NB; ++u) {
+            const int p = p0 + u, r = p * 4 + wave, t = tb + 4 * p;
+            if (p >= nrow || !qk) continue;
+            const f32x4 v = rotate4(st[r * 64 + (lane ^ (r & 63))], cs[u], sn[u]);
+            if (f < HD) {
+              store_head4(reinterpret_cast<bf16*>(a.q_out) + (size_t)t * HD + (f - dd), dd, v * qs, a.rope_half, D);
+            } else {
+              const int pos = __builtin_amdgcn_readlane(pos_l, p);
+              const size_t blk = (size_t)__builtin_amdgcn_readlane(blk_l, p);
+              store_head4(reinterpret_cast<bf16*>(a.cache.k_pool) + ((blk * G + g) * 16 + (pos & 15)) * D, dd, v,
+                          a.rope_half, D);
+            }
           }
         }
       }
       // ---- pass 2: v (cache rows of V^T: 16 keys of one feature per 32 bytes) ----
-      const int vf0 = max(n0, HD + KD), vf1 = min(n0 + 256, HD + 2 * KD);
-      if (vf0 < vf1) {
+      if (has_v) {
+        const int vf0 = max(n0, HD + KD), vf1 = min(n0 + C::BN, HD + 2 * KD);
         const int nvf = vf1 - vf0;
         const int units = 8 * nvf * 2;  // 16-row groups x features x row halves
         for (int u = tid; u < units; u += 256) {
@@ -646,22 +683,15 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
           const int vfeat = n0 + fl - HD - KD, g = vfeat / D, d = vfeat - g * D;
           const int r0 = 16 * rg, t0 = m0 + hh * 128 + r0;
           if (t0 >= a.M) continue;
-          const int b0 = t0 / S;
-          const int pos0 = a.batch.desc[2 * b0 + 1] + (t0 - b0 * S);
           const int cidx = fl >> 2, e = fl & 3;
           // row r (0..127) of the half held in LDS
           auto lds_val = [&](int r) { return stf[(r * 64 + (cidx ^ (r & 63))) * 4 + e]; };
-          const bool whole = (pos0 & 15) == 0 && t0 + 15 < a.M && (t0 + 15) / S == b0;
-          if (whole) {  // keys 4ch..4ch+3 and 8+4ch..8+4ch+3 of the block starting at pos0
-            const int seq = a.batch.desc[2 * b0];
-            const size_t blk = (size_t)a.cache.block_table[(size_t)seq * a.cache.max_blocks + (pos0 >> 4)];
+          const int blk = vgrp[rg];
+          if (blk >= 0) {  // keys 4ch..4ch+3 and 8+4ch..8+4ch+3 of the group's block
             bf16x8 w;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-              const int key = 4 * ch + (k & 3) + 2 * (k & 4);
-              w[k] = from_f32<bf16>(lds_val(r0 + key) * a.rowscale[t0 + key]);
-            }
-            *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.cache.v_pool) + ((blk * G + g) * D + d) * 16 +
+            for (int k = 0; k < 8; ++k) w[k] = from_f32<bf16>(lds_val(r0 + 4 * ch + (k & 3) + 2 * (k & 4)));
+            *reinterpret_cast<bf16x8*>(reinterpret_cast<bf16*>(a.cache.v_pool) + (((size_t)blk * G + g) * D + d) * 16 +
                                        8 * ch) = w;
           } else {  // key by key: this unit takes rows r0 + 4ch + {0..3} and r0 + 8 + 4ch + {0..3}
 #pragma unroll
@@ -670,9 +700,9 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
               const int t = t0 + rr;
               if (t >= a.M) continue;
               const int b = t / S, pos = a.batch.desc[2 * b + 1] + (t - b * S), seq = a.batch.desc[2 * b];
-              const size_t blk = (size_t)a.cache.block_table[(size_t)seq * a.cache.max_blocks + (pos >> 4)];
-              reinterpret_cast<bf16*>(a.cache.v_pool)[((blk * G + g) * D + d) * 16 + vperm_pos(pos & 15)] =
-                  from_f32<bf16>(lds_val(r0 + rr) * a.rowscale[t]);
+              const size_t kb = (size_t)a.cache.block_table[(size_t)seq * a.cache.max_blocks + (pos >> 4)];
+              reinterpret_cast<bf16*>(a.cache.v_pool)[((kb * G + g) * D + d) * 16 + vperm_pos(pos & 15)] =
+                  from_f32<bf16>(lds_val(r0 + rr));
             }
           }
         }
