@@ -13,8 +13,13 @@ the bf16 kernels, in layer order:
     (exact when gamma_1 = 1);
   * q, k, v after the row scale and RoPE: q stored as bf16(q * log2(e)/sqrt(D))
     (scores then come out in exp2 units), k and v stored in the cache;
-  * P = exp2(s - m), rounded to bf16 as the second product's operand (the row
-    sum l is taken from the unrounded P);
+  * P = exp2(s - m), rounded to bf16 as the second product's operand; the
+    row sum l adds the same rounded values.  The kernels take m as the
+    running maximum of the keys seen so far (online softmax; the prefill
+    kernel also keeps a stale maximum until the row's scores grow by 2^8), so
+    P is rounded at a scale 2^(m_final - m) that is not a power of two: a
+    realisation (below) rounds each row's P in 64-key tiles at a random
+    scale 2^u, u ~ U(0, 1), and divides it out again;
   * the attention output o / l;
   * h * gamma_2 as the gate/up operand (h itself stays fp32);
   * s = SiLU(r2 g) * (r2 u);
@@ -34,10 +39,46 @@ import oracle
 
 LOG2E = 1.4426950408889634
 
+# Realisations.  The kernels compute between their bf16 roundings in fp32,
+# whose accumulation order shifts each value by a relative 1e-7 .. 1e-6; that
+# decides which values near a rounding boundary round up or down, so the
+# kernels' error is one draw from a distribution the model can sample: with a
+# generator set, every value is scaled by (1 + u * PERTURB_EPS), u ~ U(-1, 1),
+# before each bf16 rounding (2^-18 is the size of fp32 rounding accumulated
+# over the 4096-term dot products).  None: the plain model.
+PERTURB_EPS = 2.0 ** -18
+_perturb_rng = None
 
-def rb(a: np.ndarray, on: bool = True) -> np.ndarray:
-    """Round to bf16, nearest-even (identity when on is False)."""
-    return oracle.round_storage(a, "bf16") if on else np.asarray(a, dtype=np.float64)
+
+def set_realisation(seed):
+    """Perturb the values before each rounding with a generator of this seed (None: off)."""
+    global _perturb_rng
+    _perturb_rng = None if seed is None else np.random.Generator(np.random.PCG64(seed))
+
+
+def rb(a: np.ndarray, on: bool = True, accumulated: bool = True) -> np.ndarray:
+    """Round to bf16, nearest-even (identity when on is False).  `accumulated`:
+    the value comes out of fp32 accumulation on the GPU, so a realisation
+    perturbs it first (the weight fold W * gamma is one fp32 product: not)."""
+    if not on:
+        return np.asarray(a, dtype=np.float64)
+    a = np.asarray(a, dtype=np.float64)
+    if _perturb_rng is not None and accumulated:
+        a = a * (1.0 + PERTURB_EPS * _perturb_rng.uniform(-1.0, 1.0, size=a.shape))
+    return oracle.round_storage(a, "bf16")
+
+
+P_TILE = 64  # keys that share one rounding scale of P in a realisation
+
+
+def _round_p(p: np.ndarray, on: bool) -> np.ndarray:
+    """P rounded to bf16: at the final row maximum (plain model), or in a
+    realisation at a random scale 2^u per row and 64-key tile."""
+    if not on or _perturb_rng is None:
+        return rb(p, on, accumulated=False)
+    nt = -(-p.shape[1] // P_TILE)
+    c = np.repeat(np.exp2(_perturb_rng.uniform(0.0, 1.0, size=(p.shape[0], nt))), P_TILE, axis=1)[:, :p.shape[1]]
+    return rb(p * c, True, accumulated=False) / c
 
 
 def _attention(qs, k, v, q_pos, k_pos, round_p: bool):
@@ -51,8 +92,8 @@ def _attention(qs, k, v, q_pos, k_pos, round_p: bool):
         g = h // R
         s = qs[:, h, :] @ k[:, g, :].T
         s = np.where(visible, s, -np.inf)
-        p = np.exp2(s - np.max(s, axis=1, keepdims=True))
-        out[:, h, :] = (rb(p, round_p) @ v[:, g, :]) / np.sum(p, axis=1, keepdims=True)
+        p = _round_p(np.exp2(s - np.max(s, axis=1, keepdims=True)), round_p)
+        out[:, h, :] = (p @ v[:, g, :]) / np.sum(p, axis=1, keepdims=True)
     return out
 
 
@@ -75,7 +116,7 @@ def layer_forward(cfg: dict, w: dict, x: np.ndarray, start_pos: int = 0, past_k=
     r1 = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
 
     def proj(name):
-        return r1 * (x @ rb(w[name] * g1, round).T)
+        return r1 * (x @ rb(w[name] * g1, round, accumulated=False).T)
 
     k = oracle.apply_rope(proj("k_proj").reshape(T, G, D), pos, cfg["rope_theta"], style)
     k = rb(k, round)
@@ -126,7 +167,7 @@ def stack_prefill(cfg, layers, final_gamma, x, round=True):
         kb, vb = [], []
         for w in layers:
             out, k, v = layer_forward(cfg, w, h, 0, round=round)
-            h = rb(out, True)  # the stack's storage rounding, present in the oracle too
+            h = rb(out, True)  # the stack's storage rounding (the oracle rounds its own hidden state too)
             kb.append(k)
             vb.append(v)
         ys.append(oracle.rms_norm(h, final_gamma, cfg["rms_norm_eps"]))

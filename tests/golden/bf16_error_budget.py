@@ -43,6 +43,31 @@ def _weights(w, gamma_std=None, layer=0):
     return {k: synth.as_f64(v) for k, v in ws.items()}
 
 
+REALISATIONS = 16  # perturbed draws of the model per case (tests/bf16_model.py set_realisation)
+
+
+def over_realisations(compute):
+    """Errors of the plain model and of REALISATIONS perturbed draws: `compute()`
+    returns {case: (model output, oracle output)}; the result per case holds the
+    largest max and mean over the draws and the plain model's own errors."""
+    out = {}
+    for r in range(REALISATIONS + 1):
+        M.set_realisation(None if r == 0 else 1000 + r)
+        try:
+            pairs = compute()
+        finally:
+            M.set_realisation(None)
+        for case, (got, ref) in pairs.items():
+            e = errors(got, ref)
+            ent = out.setdefault(case, {"max_rel": 0.0, "mean_rel": 0.0, "draws": []})
+            ent["max_rel"] = max(ent["max_rel"], e["max_rel"])
+            ent["mean_rel"] = max(ent["mean_rel"], e["mean_rel"])
+            ent["draws"].append([e["max_rel"], e["mean_rel"]])
+            if r == 0:
+                ent["plain"] = e
+    return out
+
+
 def stack3(_):
     """The bf16 stack case: LLaMA-3-8B shape, B 2, S 300, 3 layers, prefill + 2 decode steps."""
     w = synth.scaled(W[3], batch=2, seq_len=300)
@@ -51,28 +76,34 @@ def stack3(_):
     wo = [_weights(w, None, l) for l in range(NL)]
     gf = synth.as_f64(synth.final_norm_weight(w))
     x = synth.as_f64(synth.layer_input(w))
-    res = {"case": "llama3-8b shape, B 2, S 300, 3 layers (prefill f32 out, 2 decode steps bf16 out)"}
     ref, k_ref, v_ref = oracle.stack_prefill(cfg, wo, gf, x, "bf16")
-    got, k_m, v_m = M.stack_prefill(cfg, wo, gf, x)
-    res["prefill"] = errors(got, ref)
-    res["last_layer_k"] = errors(k_m[NL - 1, 1], k_ref[NL - 1, 1])
-    res["last_layer_v"] = errors(v_m[NL - 1, 1], v_ref[NL - 1, 1])
-    # a single layer on the same input (the first layer of the stack)
     o1, _, _ = oracle.prefill(cfg, wo[0], x)
-    m1, _, _ = M.prefill(cfg, wo[0], x)
-    res["single_layer_prefill"] = errors(m1, o1)
+    steps = []
     c_ref = [[(k_ref[l, b], v_ref[l, b]) for b in range(w.batch)] for l in range(NL)]
-    c_m = [[(k_m[l, b], v_m[l, b]) for b in range(w.batch)] for l in range(NL)]
     for step in range(2):
         xt = synth.as_f64(synth.decode_input(w, step))
         r, c_ref = oracle.stack_decode_step(cfg, wo, gf, xt, c_ref, "bf16")
-        g, c_m = M.stack_decode_step(cfg, wo, gf, xt, c_m, out_bf16=True)
-        res[f"decode_step{step}"] = errors(g, r)
+        steps.append((xt, r))
+
+    def compute():
+        got, k_m, v_m = M.stack_prefill(cfg, wo, gf, x)
+        m1, _, _ = M.prefill(cfg, wo[0], x)
+        res = {"prefill": (got, ref), "last_layer_k": (k_m[NL - 1, 1], k_ref[NL - 1, 1]),
+               "last_layer_v": (v_m[NL - 1, 1], v_ref[NL - 1, 1]), "single_layer_prefill": (m1, o1)}
+        c_m = [[(k_m[l, b], v_m[l, b]) for b in range(w.batch)] for l in range(NL)]
+        for step, (xt, r) in enumerate(steps):
+            g, c_m = M.stack_decode_step(cfg, wo, gf, xt, c_m, out_bf16=True)
+            res[f"decode_step{step}"] = (g, r)
+        return res
+
+    res = over_realisations(compute)
+    res["case"] = "llama3-8b shape, B 2, S 300, 3 layers (prefill f32 out, 2 decode steps bf16 out)"
     return res
 
 
 def gamma_rows(args):
-    """gamma ~ 1 + N(0, 0.1^2), LLaMA-3-8B shape, B 1, by sequence length (row samples past S 300)."""
+    """gamma ~ 1 + N(0, 0.1^2), LLaMA-3-8B shape, B 1, by sequence length (row
+    samples past S 300); the 300-token case (a GPU test) over realisations."""
     out = {}
     for S in args.gamma_lengths:
         w = synth.scaled(W[3], batch=1, seq_len=S)
@@ -83,8 +114,11 @@ def gamma_rows(args):
         for tag, gstd in (("gamma", 0.1), ("gamma_one", None)):
             wo = _weights(w, gstd)
             ref, _, _ = oracle.prefill(cfg, wo, x, rows=rows)
-            got, _, _ = M.prefill(cfg, wo, x, rows=rows)
-            ent[tag] = errors(got, ref)
+            if S == 300 and tag == "gamma":
+                ent[tag] = over_realisations(lambda: {"e": (M.prefill(cfg, wo, x, rows=rows)[0], ref)})["e"]
+            else:
+                got, _, _ = M.prefill(cfg, wo, x, rows=rows)
+                ent[tag] = errors(got, ref)
         out[str(S)] = ent
         print("gamma", S, ent, flush=True)
     return out
@@ -99,8 +133,7 @@ def short_prompts(_):
         wo = _weights(w)
         x = synth.as_f64(synth.layer_input(w))
         ref, _, _ = oracle.prefill(cfg, wo, x)
-        got, _, _ = M.prefill(cfg, wo, x)
-        out[f"B{B}_S{S}"] = errors(got, ref)
+        out[f"B{B}_S{S}"] = over_realisations(lambda: {"e": (M.prefill(cfg, wo, x)[0], ref)})["e"]
         print("short", B, S, out[f"B{B}_S{S}"], flush=True)
     return out
 
