@@ -67,6 +67,11 @@ def errors(gpu, ref) -> dict:
 
 def assert_close(gpu, ref, dtype: str, what: str = "") -> dict:
     e = errors(gpu, ref)
+    log = os.environ.get("PARITY_LOG")
+    if log:  # one JSON line per comparison: the measured errors beside the bound
+        with open(log, "a") as f:
+            test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+            f.write(json.dumps({"test": test, "what": what, "tol": dtype, "bound": TOL[dtype], **e}) + "\n")
     assert e["finite"], f"{what}: non-finite GPU output"
     for k, lim in TOL[dtype].items():
         assert e[k] <= lim, f"{what}: {k}={e[k]:.3e} > {lim:.1e} ({e})"
