@@ -183,6 +183,85 @@ def run_prefill(args, torch, L, synth):
     return w, res
 
 
+def run_other_workloads(args, torch, L, synth):
+    """Quick timings of the other workload definitions, so that their numbers
+    reach the result line: the tiny fp32 layer's prefill and decode-step
+    latency, and the LLaMA-7B and LLaMA-3-70B layer prefills (wall clock
+    around back-to-back calls with inputs in HBM, no per-kernel events)."""
+    out = {}
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    # tiny fp32 layer: B 1, S 64 prefill, then decode steps against its cache
+    w = synth.WORKLOADS[1]
+    layer = L.DecoderLayer(w.config_dict(), synth.layer_weights(w), w.dtype, w.positions_needed())
+    cache = L.PagedKVCache(layer, w.batch * ((w.positions_needed() + 15) // 16), w.batch)
+    x = synth.layer_input(w).cuda()
+    xt = synth.decode_input(w, 0).cuda()
+
+    def prefill():
+        sids = [cache.add_seq() for _ in range(w.batch)]
+        layer.prefill(cache, sids, x)
+        return sids
+
+    def prefill_free():
+        for s in prefill():
+            cache.free_seq(s)
+
+    pre_ms = timed(prefill_free, 50, 5)
+    dec_us = []
+    for _ in range(10):  # each round: prefill, then the workload's decode steps, timed one by one
+        sids = prefill()
+        torch.cuda.synchronize()
+        for _ in range(w.decode_steps):
+            t0 = time.perf_counter()
+            layer.decode(cache, sids, xt)
+            torch.cuda.synchronize()
+            dec_us.append((time.perf_counter() - t0) * 1e6)
+        for s in sids:
+            cache.free_seq(s)
+    cache.close()
+    layer.close()
+    out[w.name] = {"prefill_ms": round(pre_ms, 4), "decode_us_per_step": round(float(np.median(dec_us)), 1),
+                   "batch": w.batch, "seq_len": w.seq_len, "decode_steps": w.decode_steps,
+                   "note": "latency of single calls, each synchronised (launch-bound at this size)"}
+    log(f"[bench] {w.name}: prefill {pre_ms:.3f} ms, decode step {np.median(dec_us):.1f} us")
+
+    for name in ("llama-7b-layer-prefill", "llama3-70b-layer-prefill"):
+        w = synth.PREFILL_JOBS[name]
+        log(f"[bench] {name}: generating weights")
+        layer = L.DecoderLayer(w.config_dict(), synth.layer_weights(w), "bf16", w.positions_needed())
+        cache = L.PagedKVCache(layer, w.batch * ((w.seq_len + 15) // 16), w.batch)
+        x = synth.layer_input(w).cuda()
+        y = torch.empty((w.batch, w.seq_len, w.hidden_size), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            sids = [cache.add_seq() for _ in range(w.batch)]
+            layer.prefill(cache, sids, x, out_dtype="bf16", out=y)
+            for s in sids:
+                cache.free_seq(s)
+
+        ms = timed(step, min(args.steps, 10), 2)
+        fl = sum(prefill_flops(w).values())
+        out[name] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(w.batch * w.seq_len / (ms * 1e-3), 1),
+                     "layer_tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                     "layer_mfma_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "batch": w.batch, "seq_len": w.seq_len}
+        log(f"[bench] {name}: {ms:.3f} ms/step")
+        cache.close()
+        layer.close()
+        del x, y
+    return out
+
+
 def run_decode(args, torch, L, synth):
     w = synth.DECODE_JOBS[args.decode_workload]
     log(f"[bench] decode workload {w.name}: weights and cache")
@@ -336,6 +415,8 @@ def main():
     ap.add_argument("--decode-warmup", type=int, default=4)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the quick timings of the tiny fp32, LLaMA-7B and LLaMA-3-70B layers")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="oracle rows (>= S: the whole layer)")
     ap.add_argument("--prefill-workload", default="llama3-8b-layer-prefill", choices=sorted(synth.PREFILL_JOBS))
     ap.add_argument("--decode-workload", default="llama3-8b-layer-decode", choices=sorted(synth.DECODE_JOBS))
@@ -358,6 +439,7 @@ def main():
 
     w, pre = run_prefill(args, torch, L, synth)
     dec = None if args.no_decode else run_decode(args, torch, L, synth)
+    other = None if args.no_other_workloads else run_other_workloads(args, torch, L, synth)
     cpu = None if args.no_cpu_baseline else cpu_baseline(synth, w, args.cpu_rows)
     line = {
         "metric": METRIC, "value": round(pre["tokens_per_s"], 1), "unit": "tokens/s", "n_gpus": 1,
@@ -375,6 +457,7 @@ def main():
         "layer_roofline": pre["layer_roofline"],
         "kernels": pre["kernels"],
         "decode": dec,
+        "other_workloads": other,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
