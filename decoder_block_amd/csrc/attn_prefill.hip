@@ -70,9 +70,16 @@ DEVI int k_swz(int row) { return row & (CPRK - 1) & 15; }
 template <int VROW>
 DEVI int v_swz(int d) { return (d >> 1) & 7; }
 
-// Lazy rescaling: the running max of a row is only raised when a new score
-// exceeds it by more than 2^8 in exp2 units, so unnormalised P stays <= 256.
+// Lazy rescaling (fp32 kernel): the running max of a row is only raised when
+// a new score exceeds it by more than 8 in exp2 units, so unnormalised P
+// stays <= 256.
 constexpr float kRescaleLog2 = 8.f;
+// bf16 kernel: the running max starts at 0 and rises only when a score
+// exceeds it by more than kRiseLog2 (unnormalised P <= 2^32); on the first
+// tile also when the row's max is below -kLowLog2 (its largest P stays a
+// normal number).
+constexpr float kRiseLog2 = 32.f;
+constexpr float kLowLog2 = 64.f;
 
 template <typename T, int D>
 __global__ __launch_bounds__(512) void attn_prefill_f32_kernel(const T* __restrict__ q, T* __restrict__ attn,
@@ -420,7 +427,11 @@ __global__ __launch_bounds__(512) void attn_prefill_f32_kernel(const T* __restri
 //    products, one max and rescale decision per tile, then the second half's
 //    exponentials overlap the first half's O^T product in the matrix core.
 //    The causal mask is applied only on the tiles that reach a row's
-//    diagonal (a separate copy of the tile loop).  P is rounded to
+//    diagonal (a separate copy of the tile loop).  The running max starts
+//    at 0 and moves only for scores far from it, and until it moves for
+//    some row of the wave the tiles take a copy of the loop that feeds the
+//    scores to exp2 unshifted (32 fewer VALU instructions per tile and
+//    wave: 974-990 -> 1007 TFLOP/s in the 8B layer).  P is rounded to
 //    bf16 for the O^T product and the row sum adds those same bf16 values.
 // ---------------------------------------------------------------------------
 template <int D>
@@ -575,8 +586,14 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
   // P registers hold)
   const int vaddr = C::TILE + l32 * 32 + ((hl ^ ((l32 >> 3) & 1)) * 16);
 
-  float m_run = 0.f, l_run = 0.f;  // m_run: running max in exp2 units (valid once `first` is false)
-  bool first = true;
+  // m_run: the row's running max in exp2 units, raised lazily (below).  It
+  // starts at 0 and stays there while the row's first-tile max lies in
+  // [-kLowLog2, kRiseLog2] and no later score exceeds kRiseLog2; while every
+  // row of the wave has m_run = 0 the tiles take a copy that feeds the scores
+  // to exp2 with no subtraction.  `shifted` (wave-uniform) is set once some
+  // row's m_run moved.
+  float m_run = 0.f, l_run = 0.f;
+  bool first = true, shifted = false;
   f32x16 o[C::NDB];
 #pragma unroll
   for (int db = 0; db < C::NDB; ++db)
@@ -603,8 +620,9 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
   // diagonal (DIAG) apply the causal mask.
   const char* lds = reinterpret_cast<const char*>(ring);
   const bf16x2 ones2 = {from_f32<bf16>(1.f), from_f32<bf16>(1.f)};
-  auto tile = [&](const char* sb, int k0, auto diag_) {
+  auto tile = [&](const char* sb, int k0, auto diag_, auto shift_) {
     constexpr bool DIAG = decltype(diag_)::value;
+    constexpr bool SHIFT = decltype(shift_)::value;  // some row of the wave has m_run != 0
     auto kfrag = [&](int kb, int kk) {
       return *reinterpret_cast<const bf16x8*>(sb + kaddr[kk] + kb * 32 * C::CPRK * 16);
     };
@@ -678,23 +696,36 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
       mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
     }
     // the running max m is raised lazily: only when a score exceeds it by
-    // more than 2^8, so unnormalised P stays <= 256; the final division uses
-    // the same stale max, so the result is exact
-    const bool grow = first || mx - m_run > kRescaleLog2;
+    // more than kRiseLog2 (so unnormalised P stays <= 2^32, and the sums of
+    // P and of P V stay far inside fp32), or, on the first tile, when the
+    // row's max lies outside [-kLowLog2, kRiseLog2] (so that the largest P of
+    // every row is a normal number); the final division uses the same stale
+    // max, so the result is exact.  The bf16 rounding of P is relative, so
+    // the shift does not change its precision.
+    const bool grow = first ? (mx > kRiseLog2 || mx < -kLowLog2) : mx - m_run > kRiseLog2;
     if (wave_any(grow)) {
       const float m_new = grow ? mx : m_run;
-      const float alpha = first ? 0.f : fast_exp2(m_run - m_new);
+      const float alpha = first ? 0.f : fast_exp2(m_run - m_new);  // first tile: o and l are 0
+      if constexpr (!SHIFT) {  // m_run was 0: this tile's exponents are s - m_new
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          sc0[i] -= m_new;
+          sc1[i] -= m_new;
+        }
+      }
       m_run = m_new;
-      first = false;
+      shifted = shifted || wave_any(m_run != 0.f);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) o[db] *= alpha;
     }
+    first = false;
     // P in bf16 (the O^T product's operand); the row sum adds the same bf16
     // values, so O / l is a weighted mean of V with weights summing to one
+    auto expo = [&](float sv) { return SHIFT ? sv - m_run : sv; };
     bf16x8 p0[2], p1[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p0[i >> 3][i & 7] = from_f32<bf16>(fast_exp2(sc0[i] - m_run));
+    for (int i = 0; i < 16; ++i) p0[i >> 3][i & 7] = from_f32<bf16>(fast_exp2(expo(sc0[i])));
     __builtin_amdgcn_sched_barrier(0);
     // stage 5: O^T += V^T P^T for the first half || exponentials of the second
     // half, V^T fragments of the second half
@@ -708,7 +739,7 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) va1[m][db] = vfrag(1, m, db);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p1[i >> 3][i & 7] = from_f32<bf16>(fast_exp2(sc1[i] - m_run));
+    for (int i = 0; i < 16; ++i) p1[i >> 3][i & 7] = from_f32<bf16>(fast_exp2(expo(sc1[i])));
 #pragma unroll
     for (int kk = 0; kk < 2 * C::NDB; ++kk) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -741,14 +772,14 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
   // One iteration of the tile loop: the next DMA into the freed slot, the
   // tile (skipped when it is past every row of this wave), then the wait for
   // the next tile and the barrier that publishes it.
-  auto step = [&](int kt, auto diag) {
+  auto step = [&](int kt, auto diag, auto shift) {
     const int st = kt % C::NST;
     const int k0 = kt * C::KT;
     if (kt + C::NST - 1 < ntiles) {
       issue((kt + C::NST - 1) % C::NST, bk_next);
       bk_next = block_of(min(kt + C::NST, ntiles - 1));
     }
-    if (k0 <= wmax) tile(lds + st * C::SLOT, k0, diag);
+    if (k0 <= wmax) tile(lds + st * C::SLOT, k0, diag, shift);
     if (kt + 1 < ntiles) {
       wait_tile(kt + 1);
       finish(kt + 1, (kt + 1) % C::NST);
@@ -762,8 +793,11 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
   // which keeps the register allocation of each free of the other.
   const int kt_diag = min(ntiles, wmin >= C::KT - 1 ? (wmin - (C::KT - 1)) / C::KT + 1 : 0);
   int kt = 0;
-  for (; kt < kt_diag; ++kt) step(kt, std::false_type{});
-  for (; kt < ntiles; ++kt) step(kt, std::true_type{});
+  // (and a loop without the shift by m_run until some row's m_run moves)
+  for (; kt < kt_diag && !shifted; ++kt) step(kt, std::false_type{}, std::false_type{});
+  for (; kt < kt_diag; ++kt) step(kt, std::false_type{}, std::true_type{});
+  for (; kt < ntiles && !shifted; ++kt) step(kt, std::true_type{}, std::false_type{});
+  for (; kt < ntiles; ++kt) step(kt, std::true_type{}, std::true_type{});
 
   if (!active) return;
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);

@@ -14,10 +14,11 @@ the bf16 kernels, in layer order:
   * q, k, v after the row scale and RoPE: q stored as bf16(q * log2(e)/sqrt(D))
     (scores then come out in exp2 units), k and v stored in the cache;
   * P = exp2(s - m), rounded to bf16 as the second product's operand; the
-    row sum l adds the same rounded values.  The kernels take m as the
+    row sum l adds the same rounded values.  The kernels take m as a
     running maximum of the keys seen so far (online softmax; the prefill
-    kernel also keeps a stale maximum until the row's scores grow by 2^8), so
-    P is rounded at a scale 2^(m_final - m) that is not a power of two: a
+    kernel keeps it at 0, or stale, until a score exceeds it by 32 in exp2
+    units), so P is rounded at a scale 2^(m_final - m) that is not a power
+    of two: a
     realisation (below) rounds each row's P in 64-key tiles at a random
     scale 2^u, u ~ U(0, 1), and divides it out again;
   * the attention output o / l;

@@ -138,7 +138,23 @@ def short_prompts(_):
     return out
 
 
-PARTS = {"stack3": stack3, "gamma_by_length": gamma_rows, "short_prompts": short_prompts}
+def score_ranges(_):
+    """Attention scores far from 0 (tests/score_cases.py): the 8B shape, B 1, S 300."""
+    from tests import score_cases as SC
+    out = {}
+    for name in SC.CASES:
+        w, ws, x = SC.score_case(name)
+        cfg = w.config_dict()
+        wo = {k: synth.as_f64(v) for k, v in ws.items()}
+        xx = synth.as_f64(x)
+        ref, _, _ = oracle.prefill(cfg, wo, xx)
+        out[name] = over_realisations(lambda: {"e": (M.prefill(cfg, wo, xx)[0], ref)})["e"]
+        print("scores", name, out[name]["max_rel"], out[name]["mean_rel"], flush=True)
+    return out
+
+
+PARTS = {"stack3": stack3, "gamma_by_length": gamma_rows, "short_prompts": short_prompts,
+         "score_ranges": score_ranges}
 
 
 def main():

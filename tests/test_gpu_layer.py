@@ -269,6 +269,23 @@ def test_bf16_short_prompts(B, S):
     print("short prompt", B, S, e)
 
 
+@pytest.mark.parametrize("name", ["qk_x2", "qk_x4", "all_high", "all_low"])
+def test_bf16_attention_scores_far_from_zero(name):
+    # the prefill attention's running max starts at 0 and moves only for
+    # scores outside [-64, 32] (exp2 units): these inputs take every branch
+    # of that (a rise on a later tile, a rise on the first tile, all scores
+    # about +100 or about -100); tests/score_cases.py builds them
+    from tests import score_cases as SC
+    w, ws, x = SC.score_case(name)
+    layer = P.make_layer(w, ws)
+    cache = P.make_cache(layer, w, w.seq_len, w.batch)
+    out, sids = P.gpu_prefill(layer, cache, x)
+    wo = {k: synth.as_f64(v) for k, v in ws.items()}
+    ref, k_ref, _ = oracle.prefill(_cfg(w), wo, synth.as_f64(x))
+    e = P.assert_close(P.to_np(out), ref, P.model_tol(f"score_ranges/{name}"), f"scores far from 0: {name}")
+    print("scores far from 0", name, e)
+
+
 def test_cache_restore_gives_identical_decode():
     w = synth.scaled(W[3], batch=1, seq_len=100)
     ws, _ = P.weights_for(w)
