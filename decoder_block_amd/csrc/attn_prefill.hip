@@ -454,7 +454,8 @@ struct BCfg {
 
 template <int D>
 __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __restrict__ q, bf16* __restrict__ attn,
-                                                                int H, CacheView cache, BatchView batch) {
+                                                                int H, CacheView cache, BatchView batch,
+                                                                int paired) {
   using C = BCfg<D>;
   __shared__ u32x4 ring[C::NST * C::SLOT / 16];
 
@@ -463,8 +464,6 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
   const int P = C::ROWS / R;  // positions per workgroup
   const int S = batch.seq_len;
   const int b = blockIdx.x / G, g = blockIdx.x % G;
-  const int nrb = (S + P - 1) / P;
-  const int rb = nrb - 1 - (int)blockIdx.y;
   const int seq = batch.desc[2 * b];
   const int start = batch.desc[2 * b + 1];
   const int kv_len = start + S;
@@ -475,11 +474,35 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
   const int hl = lane >> 5, l32 = lane & 31;
 
   // query row j of the workgroup -> (head, sequence index); rows past the end
-  // mirror the block's first row (computed, never stored)
+  // mirror a row of the workgroup that exists (computed, never stored).
+  // Plain: the workgroup takes the P positions of block rb of its R heads.
+  // Paired (for launches of at most one workgroup per CU, where the longest
+  // causal row block would set the time): the sequence is cut into half
+  // blocks of P/2 positions, and workgroup y takes half block nhb-1-y on
+  // waves 0-3 and half block y on waves 4-7, so every workgroup does the
+  // same causal work; once the short half is done, each SIMD runs one wave.
   const int j = wave * 32 + l32;
-  const int head = g * R + j / P;
-  const bool active = rb * P + j % P < S;
-  const int sidx = active ? rb * P + j % P : rb * P;
+  int head, pidx, last_s, first_s;
+  bool active;
+  if (!paired) {
+    const int nrb = (S + P - 1) / P;
+    const int rb = nrb - 1 - (int)blockIdx.y;
+    head = g * R + j / P;
+    pidx = rb * P + j % P;
+    active = pidx < S;
+    first_s = rb * P;
+    last_s = min(S, (rb + 1) * P) - 1;
+  } else {
+    const int HP = P / 2, nhb = (S + HP - 1) / HP;
+    const int hb_long = nhb - 1 - (int)blockIdx.y, hb_short = (int)blockIdx.y;
+    const int half = j / (C::ROWS / 2), jj = j % (C::ROWS / 2);
+    head = g * R + jj / HP;
+    pidx = (half ? hb_short : hb_long) * HP + jj % HP;
+    active = pidx < S && !(half && hb_short == hb_long);  // odd nhb: the middle half block once
+    first_s = hb_long * HP;
+    last_s = min(S, (hb_long + 1) * HP) - 1;
+  }
+  const int sidx = active ? pidx : first_s;
   const int qpos = start + sidx;
   int wmax = qpos, wmin = qpos;
 #pragma unroll
@@ -489,7 +512,6 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
   }
   wmax = __builtin_amdgcn_readfirstlane(wmax);
   wmin = __builtin_amdgcn_readfirstlane(wmin);
-  const int last_s = min(S, (rb + 1) * P) - 1;
   const int ntiles = (start + last_s) / C::KT + 1;
 
   // Q fragments (B operand of S^T), resident for the whole key loop
@@ -815,18 +837,35 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
     }
 }
 
+// Compute units of the current device (the launch shape below depends on
+// whether a launch fills them more than once).
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 template <typename T, int D>
 hipError_t launch_d(const void* q, void* attn, int H, const CacheView& c, const BatchView& b, hipStream_t s) {
   const int R = H / c.G;
   const int P = ACfg<T, D>::ROWS / R;
   static_assert(ACfg<T, D>::ROWS == BCfg<D>::ROWS, "same rows per workgroup");
-  dim3 grid(c.G * b.batch, (b.seq_len + P - 1) / P);
-  if constexpr (sizeof(T) == 2)
+  const int nrb = (b.seq_len + P - 1) / P;
+  if constexpr (sizeof(T) == 2) {
+    // one workgroup per CU at a time: a launch within one round takes the
+    // paired row blocks (equal causal work per workgroup)
+    const bool paired = nrb > 1 && c.G * b.batch * nrb <= cu_count();
+    const int HP = P / 2;
+    dim3 grid(c.G * b.batch, paired ? ((b.seq_len + HP - 1) / HP + 1) / 2 : nrb);
     attn_prefill_bf16_kernel<D><<<grid, BCfg<D>::NT, 0, s>>>(reinterpret_cast<const bf16*>(q),
-                                                             reinterpret_cast<bf16*>(attn), H, c, b);
-  else
+                                                             reinterpret_cast<bf16*>(attn), H, c, b, paired ? 1 : 0);
+  } else {
+    dim3 grid(c.G * b.batch, nrb);
     attn_prefill_f32_kernel<T, D><<<grid, ACfg<T, D>::NT, 0, s>>>(reinterpret_cast<const T*>(q),
                                                                   reinterpret_cast<T*>(attn), H, c, b);
+  }
   return hipGetLastError();
 }
 
