@@ -712,11 +712,7 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
     mask(sc1, 1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc1[i]);
-    {  // max with lane l ^ 32 (the row's other 32 keys)
-      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, mx),
-                                                       __builtin_bit_cast(unsigned, mx), false, false);
-      mx = fmaxf(__builtin_bit_cast(float, sw[0]), __builtin_bit_cast(float, sw[1]));
-    }
+    mx = max_lane_halves(mx, hl);  // with lane l ^ 32 (the row's other 32 keys)
     // the running max m is raised lazily: only when a score exceeds it by
     // more than kRiseLog2 (so unnormalised P stays <= 2^32, and the sums of
     // P and of P V stay far inside fp32), or, on the first tile, when the

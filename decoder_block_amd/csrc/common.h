@@ -158,6 +158,20 @@ __device__ __forceinline__ void buf_dma16_async(i32x4 rsrc, const void* lds_base
 }
 __device__ __forceinline__ bool wave_any(bool p) { return __any(p); }
 
+// Maximum of v over lanes l and l ^ 32 (hl = l >> 5).  v_permlane32_swap
+// exchanges the upper 32 lanes of its first operand with the lower 32 lanes of
+// its second.  Given the same value as both operands, the compiler takes the
+// two results to be equal and keeps only the first, so the maximum would see
+// one lane half only; each half is therefore swapped against a zero register:
+// lanes 0-31 find lane l + 32's value in the second result of the first swap,
+// lanes 32-63 find lane l - 32's in the first result of the second.
+DEVI float max_lane_halves(float v, int hl) {
+  const unsigned a = __builtin_bit_cast(unsigned, v);
+  const auto lo = __builtin_amdgcn_permlane32_swap(a, 0u, false, false);
+  const auto hi = __builtin_amdgcn_permlane32_swap(0u, a, false, false);
+  return fmaxf(v, __builtin_bit_cast(float, hl ? hi[0] : lo[1]));
+}
+
 // Exchange with lane l ^ m within a wave (m < 64).
 DEVI float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 

@@ -269,12 +269,14 @@ def test_bf16_short_prompts(B, S):
     print("short prompt", B, S, e)
 
 
-@pytest.mark.parametrize("name", ["qk_x2", "qk_x4", "all_high", "all_low"])
+@pytest.mark.parametrize("name", ["qk_x2", "qk_x4", "all_high", "all_low", "lane_split"])
 def test_bf16_attention_scores_far_from_zero(name):
     # the prefill attention's running max starts at 0 and moves only for
     # scores outside [-64, 32] (exp2 units): these inputs take every branch
     # of that (a rise on a later tile, a rise on the first tile, all scores
-    # about +100 or about -100); tests/score_cases.py builds them
+    # about +100 or about -100), and the last puts the high scores on the
+    # keys of one lane half only (a row maximum must see both halves);
+    # tests/score_cases.py builds them
     from tests import score_cases as SC
     w, ws, x = SC.score_case(name)
     layer = P.make_layer(w, ws)
