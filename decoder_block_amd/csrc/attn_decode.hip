@@ -484,8 +484,45 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(const float* _
   const int kv_len = batch.desc[2 * b + 1] + 1;
   const int ns = (kv_len + kChunkKeys - 1) / kChunkKeys;
   const float* p = part + (size_t)bh * max_splits * (D + 2);
-  // The splits' maxima and sums are fetched one split per lane, all at once,
-  // so the pass costs two rounds of load latency, not two per split.
+  // Up to kFew splits (contexts up to 8192 keys): every value the merge needs
+  // is loaded before any is used, one round of load latency in all; the sums
+  // run in split order, as in the general path below.
+  constexpr int kFew = 8;
+  if (ns <= kFew) {
+    float mv[kFew], lv[kFew], av[kFew][D / 64];
+#pragma unroll
+    for (int s = 0; s < kFew; ++s) {
+      const float* ps = p + min(s, ns - 1) * (D + 2);  // in bounds for every s (ns <= max_splits)
+      mv[s] = s < ns ? ps[0] : -INFINITY;
+      lv[s] = s < ns ? ps[1] : 0.f;
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) av[s][e] = s < ns ? ps[2 + lane + 64 * e] : 0.f;
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int s = 0; s < kFew; ++s) M = fmaxf(M, mv[s]);
+    float L = 0.f, acc[D / 64];
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int s = 0; s < kFew; ++s) {
+      if (s >= ns) break;
+      const float f = exp2f(mv[s] - M);
+      L += f * lv[s];
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) acc[e] += f * av[s][e];
+    }
+    const float inv = 1.f / L;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) {
+      const int col = h * D + lane + 64 * e;
+      const size_t o = sizeof(T) == 2 ? tiled_off(b, col, H * D) : (size_t)b * H * D + col;
+      attn[o] = from_f32<T>(acc[e] * inv);
+    }
+    return;
+  }
+  // More splits: their maxima and sums are fetched one split per lane, all
+  // at once, so the pass costs two rounds of load latency, not two per split.
   float M = -INFINITY;
   for (int s0 = 0; s0 < ns; s0 += 64)
     if (s0 + lane < ns) M = fmaxf(M, p[(s0 + lane) * (D + 2)]);
