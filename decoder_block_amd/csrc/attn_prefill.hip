@@ -712,7 +712,6 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
     mask(sc1, 1);
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc1[i]);
-    mx = max_lane_halves(mx, hl);  // with lane l ^ 32 (the row's other 32 keys)
     // the running max m is raised lazily: only when a score exceeds it by
     // more than kRiseLog2 (so unnormalised P stays <= 2^32, and the sums of
     // P and of P V stay far inside fp32), or, on the first tile, when the
@@ -720,8 +719,14 @@ __global__ __launch_bounds__(512) void attn_prefill_bf16_kernel(const bf16* __re
     // every row is a normal number); the final division uses the same stale
     // max, so the result is exact.  The bf16 rounding of P is relative, so
     // the shift does not change its precision.
-    const bool grow = first ? (mx > kRiseLog2 || mx < -kLowLog2) : mx - m_run > kRiseLog2;
-    if (wave_any(grow)) {
+    // mx is this lane's half of the row (32 keys).  A row whose max passes
+    // a bound has a half whose max passes it (the low bound: both halves),
+    // so the halves are tested alone, and the row max over both halves
+    // (lane l ^ 32) is taken only in the rare branch, where it decides.
+    const bool grow_half = first ? (mx > kRiseLog2 || mx < -kLowLog2) : mx - m_run > kRiseLog2;
+    if (wave_any(grow_half)) {
+      mx = max_lane_halves(mx, hl);
+      const bool grow = first ? (mx > kRiseLog2 || mx < -kLowLog2) : mx - m_run > kRiseLog2;
       const float m_new = grow ? mx : m_run;
       const float alpha = first ? 0.f : fast_exp2(m_run - m_new);  // first tile: o and l are 0
       if constexpr (!SHIFT) {  // m_run was 0: this tile's exponents are s - m_new
