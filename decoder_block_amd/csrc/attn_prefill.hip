@@ -14,12 +14,15 @@
 // wave's softmax (exp on the transcendental unit, VALU) overlap the other
 // wave's MFMAs.  Row blocks are issued latest-position first (the
 // longest causal rows start first) and the KV groups of a row block sit on
-// consecutive workgroup ids, i.e. one group per XCD.
+// consecutive workgroup ids, i.e. one group per XCD.  A launch of at most one
+// workgroup per CU instead pairs a late and an early half block of positions
+// in each workgroup, so that all of them do the same causal work.
 //
 // Per wave, transposed formulation with 32x32 MFMAs:
 //   S^T [keys x rows] = K_tile [keys x D] * Q^T        (Q resident in registers)
 //   online softmax: each lane owns one query row and 32 of the 64 scores of a
-//   tile; the row max needs one exchange with lane l^32, the running sum none
+//   tile; the row max needs one exchange with lane l^32 (only when the lazy
+//   running max may move), the running sum none
 //   O^T [D x rows]   += V_tile^T [D x keys] * P^T     (P straight from registers)
 // The cache keeps V transposed per block ([D][16 keys]), so V^T tiles are
 // staged with plain 16-byte copies.  K and V^T tiles go through a 4-slot LDS
