@@ -647,27 +647,72 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
         // row at a time, as a loop whose early exits sat before the loads,
         // cost about 45 us per QKV launch at the LLaMA-3-8B shape and 8192 tokens)
         constexpr int NB = 16;
+        // A tile of q features only (or k only) with all 32 rows and adjacent
+        // RoPE pairs (every tile of the 8B-shaped layer at 8192 tokens): the
+        // rows take no branches, so a batch's LDS reads issue together
+        // instead of one LDS round trip per row (the same values and stores
+        // as the general loop below)
+        auto rows_fast = [&](auto is_k_) {
+          constexpr bool IS_K = decltype(is_k_)::value;
 #pragma unroll 1
-        for (int p0 = 0; p0 < nrow; p0 += NB) {
-          f32x2 cs[NB], sn[NB];
+          for (int p0 = 0; p0 < 32; p0 += NB) {
+            f32x2 cs[NB], sn[NB];
+            f32x4 xr[NB];
 #pragma unroll
-          for (int u = 0; u < NB; ++u) {
-            const size_t o = (size_t)__builtin_amdgcn_readlane(pos_l, p0 + u) * (D / 2);
-            cs[u] = *reinterpret_cast<const f32x2*>(cs_col + o);
-            sn[u] = *reinterpret_cast<const f32x2*>(sn_col + o);
+            for (int u = 0; u < NB; ++u) {
+              const size_t o = (size_t)__builtin_amdgcn_readlane(pos_l, p0 + u) * (D / 2);
+              cs[u] = *reinterpret_cast<const f32x2*>(cs_col + o);
+              sn[u] = *reinterpret_cast<const f32x2*>(sn_col + o);
+            }
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+              const int r = (p0 + u) * 4 + wave;
+              xr[u] = st[r * 64 + (lane ^ (r & 63))];
+            }
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+              const int p = p0 + u, t = tb + 4 * p;
+              const f32x4 v = rotate4(xr[u], cs[u], sn[u]);
+              if constexpr (IS_K) {
+                const int pos = __builtin_amdgcn_readlane(pos_l, p);
+                const size_t blk = (size_t)__builtin_amdgcn_readlane(blk_l, p);
+                store4(reinterpret_cast<bf16*>(a.cache.k_pool) + ((blk * G + g) * 16 + (pos & 15)) * D + dd, v[0],
+                       v[1], v[2], v[3]);
+              } else {
+                const f32x4 w = v * qs;
+                store4(reinterpret_cast<bf16*>(a.q_out) + (size_t)t * HD + f, w[0], w[1], w[2], w[3]);
+              }
+            }
           }
+        };
+        const bool all_q = n0 + C::BN <= HD, all_k = n0 >= HD && n0 + C::BN <= HD + KD;
+        if (nrow == 32 && !a.rope_half && all_q) {
+          rows_fast(std::false_type{});
+        } else if (nrow == 32 && !a.rope_half && all_k) {
+          rows_fast(std::true_type{});
+        } else {
+#pragma unroll 1
+          for (int p0 = 0; p0 < nrow; p0 += NB) {
+            f32x2 cs[NB], sn[NB];
 #pragma unroll
-          for (int u = 0; u < NB; ++u) {
-            const int p = p0 + u, r = p * 4 + wave, t = tb + 4 * p;
-            if (p >= nrow || !qk) continue;
-            const f32x4 v = rotate4(st[r * 64 + (lane ^ (r & 63))], cs[u], sn[u]);
-            if (f < HD) {
-              store_head4(reinterpret_cast<bf16*>(a.q_out) + (size_t)t * HD + (f - dd), dd, v * qs, a.rope_half, D);
-            } else {
-              const int pos = __builtin_amdgcn_readlane(pos_l, p);
-              const size_t blk = (size_t)__builtin_amdgcn_readlane(blk_l, p);
-              store_head4(reinterpret_cast<bf16*>(a.cache.k_pool) + ((blk * G + g) * 16 + (pos & 15)) * D, dd, v,
-                          a.rope_half, D);
+            for (int u = 0; u < NB; ++u) {
+              const size_t o = (size_t)__builtin_amdgcn_readlane(pos_l, p0 + u) * (D / 2);
+              cs[u] = *reinterpret_cast<const f32x2*>(cs_col + o);
+              sn[u] = *reinterpret_cast<const f32x2*>(sn_col + o);
+            }
+#pragma unroll
+            for (int u = 0; u < NB; ++u) {
+              const int p = p0 + u, r = p * 4 + wave, t = tb + 4 * p;
+              if (p >= nrow || !qk) continue;
+              const f32x4 v = rotate4(st[r * 64 + (lane ^ (r & 63))], cs[u], sn[u]);
+              if (f < HD) {
+                store_head4(reinterpret_cast<bf16*>(a.q_out) + (size_t)t * HD + (f - dd), dd, v * qs, a.rope_half, D);
+              } else {
+                const int pos = __builtin_amdgcn_readlane(pos_l, p);
+                const size_t blk = (size_t)__builtin_amdgcn_readlane(blk_l, p);
+                store_head4(reinterpret_cast<bf16*>(a.cache.k_pool) + ((blk * G + g) * 16 + (pos & 15)) * D, dd, v,
+                            a.rope_half, D);
+              }
             }
           }
         }
