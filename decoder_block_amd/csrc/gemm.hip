@@ -794,21 +794,53 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
             }
       }
       __syncthreads();
+      // A half whose 128 rows all lie before M takes a copy without the
+      // per-row test, so that the LDS reads of 8 rows issue together instead
+      // of one LDS round trip per row (the same sums and stores as below).
+      auto rows_full = [&](auto out_f32_) {
+        constexpr bool OUT_F32 = decltype(out_f32_)::value;
 #pragma unroll
-      for (int p = 0; p < 32; ++p) {
-        const int r = p * 4 + wave, c = lane;  // wave-uniform row, lane = 16-byte chunk
-        const int t = m0 + hh * 128 + r;
-        if (t < a.M) {
-          const f32x4 v = st[r * 64 + (c ^ (r & 63))];
-          const size_t o = (size_t)t * a.ldo + n0 + 4 * c;
-          if constexpr (EPI == (int)Epi::RESID_H) {  // h = x + attn W_o^T, fp32
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = res[p] + v;
-          } else {  // out = h + s W_down^T
-            const f32x4 hv = res[p] + v;
-            if (a.out_dtype == DType::F32)
+        for (int p0 = 0; p0 < 32; p0 += 8) {
+          f32x4 vv[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int r = (p0 + u) * 4 + wave;
+            vv[u] = st[r * 64 + (lane ^ (r & 63))];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int p = p0 + u, r = p * 4 + wave, t = m0 + hh * 128 + r;
+            const size_t o = (size_t)t * a.ldo + n0 + 4 * lane;
+            const f32x4 hv = res[p] + vv[u];
+            if constexpr (OUT_F32)
               *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = hv;
             else
               store4(reinterpret_cast<bf16*>(a.out) + o, hv[0], hv[1], hv[2], hv[3]);
+          }
+        }
+      };
+      const bool out_f32 = EPI == (int)Epi::RESID_H || a.out_dtype == DType::F32;
+      if (m0 + hh * 128 + 128 <= a.M && out_f32) {
+        rows_full(std::true_type{});
+      } else if (m0 + hh * 128 + 128 <= a.M) {
+        rows_full(std::false_type{});
+      } else {
+#pragma unroll
+        for (int p = 0; p < 32; ++p) {
+          const int r = p * 4 + wave, c = lane;  // wave-uniform row, lane = 16-byte chunk
+          const int t = m0 + hh * 128 + r;
+          if (t < a.M) {
+            const f32x4 v = st[r * 64 + (c ^ (r & 63))];
+            const size_t o = (size_t)t * a.ldo + n0 + 4 * c;
+            if constexpr (EPI == (int)Epi::RESID_H) {  // h = x + attn W_o^T, fp32
+              *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = res[p] + v;
+            } else {  // out = h + s W_down^T
+              const f32x4 hv = res[p] + v;
+              if (a.out_dtype == DType::F32)
+                *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(a.out) + o) = hv;
+              else
+                store4(reinterpret_cast<bf16*>(a.out) + o, hv[0], hv[1], hv[2], hv[3]);
+            }
           }
         }
       }
