@@ -345,31 +345,35 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // Large bf16 tiles: 256 features x BM tokens (BM 256 or 128), four waves (one
-// per SIMD) as 2 x 2, each wave 128 features x BM/2 tokens as 4 x BM/64
-// blocks of v_mfma_f32_32x32x16_bf16 whose accumulators stay in the matrix
-// core's register file.  BM 128 is for launches that 256 x 256 tiles would
-// give fewer than two rounds of the 256 CUs (e.g. the 4096-feature
-// projections of a 2048-token prefill: 128 tiles).
-// K is staged 32 elements at a time (two k-steps of 16) in a 4-slot LDS
-// ring.  Each k-step is BM/32 slices of two MFMAs plus LDS reads of the next
-// k-step's fragments (in the order the MFMAs consume them), so with a single
-// wave per SIMD the matrix core does not wait for LDS:
-//   k-step 0 of stage kt: MFMAs || reads of k-step 1;
+// per SIMD) as 2 x 2, each wave 128 features x BM/2 tokens as 8 x BM/32
+// blocks of v_mfma_f32_16x16x32_bf16 whose accumulators stay in the matrix
+// core's register file.  The 16x16x32 form does the same work per fragment
+// read as 32x32x16 at this wave tile, but the chip holds a higher clock
+// under it (less accumulator traffic per flop), so more flops per second
+// fit the same power.  BM 128 is for launches that 256 x 256 tiles would give
+// fewer than two rounds of the 256 CUs (e.g. the 4096-feature projections of
+// a 2048-token prefill: 128 tiles).
+// K is staged 32 elements at a time (one 32-deep k-step) in a 4-slot LDS
+// ring.  A stage is BM/32 * 4 slices of four MFMAs; the slices also read the
+// next stage's fragments (in the order the MFMAs consume them) and issue the
+// DMAs of stage kt+3, so with a single wave per SIMD the matrix core does not
+// wait for LDS:
 //   wait for this wave's DMAs of stage kt+1, barrier (every wave is done
 //   with stage kt-1);
-//   last k-step: MFMAs || reads of k-step 0 of stage kt+1 || DMAs of stage
-//   kt+3 into stage kt-1's slot, spread over the slices.
-// 32x32 result layout: lane l holds token (l & 31) and, in registers
-// 4g..4g+3, features 8g + 4(l >> 5) + {0..3}: four lane-local groups of four
+//   MFMAs of stage kt || reads of stage kt+1 || DMAs of stage kt+3 into
+//   stage kt-1's slot.
+// 16x16 result layout: lane l holds token (l & 15) and features
+// 4(l >> 4) + {0..3} of its 16-feature block: a lane-local group of four
 // consecutive features, so the same epilogues apply.
 // ---------------------------------------------------------------------------
 template <int BM_>
 struct BigCfg {
-  static constexpr int BN = 256, BM = BM_, NT = 256, CPR = 4, NS = 4, KS = 2, BK = 32;
+  static constexpr int BN = 256, BM = BM_, NT = 256, CPR = 4, NS = 4, BK = 32;
   static constexpr int TW = BM / 2;                 // tokens per wave
-  static constexpr int TJ = TW / 32;                // 32-token MFMA blocks per wave
-  static constexpr int NF = 4 + TJ;                 // fragments per k-step: 4 of W, TJ of X
-  static constexpr int NSL = 2 * TJ;                // slices of two MFMAs per k-step
+  static constexpr int FI = 8;                      // 16-feature MFMA blocks per wave
+  static constexpr int TJ = TW / 16;                // 16-token MFMA blocks per wave
+  static constexpr int NF = FI + TJ;                // fragments per stage: 8 of W, TJ of X
+  static constexpr int NSL = FI * TJ / 4;           // slices of four MFMAs per stage
   static constexpr int PER = (BN + BM) * CPR / NT;  // DMAs per thread per stage
   static constexpr int SLOT = (BN + BM) * CPR;      // 16-byte chunks per slot
   static constexpr int HALVES = BM / 128;           // 128-token passes of the staged epilogues
@@ -377,6 +381,7 @@ struct BigCfg {
   // features (128 KB) at a time
   static constexpr int LDS_CHUNKS = NS * SLOT > 128 * 64 ? NS * SLOT : 128 * 64;
   static_assert(BM == 256 || BM == 128, "256 or 128 tokens per tile");
+  static_assert(TJ % 4 == 0, "a slice is four MFMAs of one W fragment");
   // 16 consecutive rows read one chunk each: the XOR spreads them over all
   // 16-byte positions of a 256-byte bank window
   static DEVI int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
@@ -389,7 +394,7 @@ struct BigCfg {
 template <int EPI, int BM>
 __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
   using C = BigCfg<BM>;
-  constexpr int NS = C::NS, TJ = C::TJ, NF = C::NF, NSL = C::NSL;
+  constexpr int NS = C::NS, TJ = C::TJ, FI = C::FI, NF = C::NF, NSL = C::NSL;
   using T = bf16;
   __shared__ u32x4 ring[C::LDS_CHUNKS];
 
@@ -446,61 +451,46 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
     buf_dma16_to(q * 64 < C::BN * C::CPR ? rW : rX, slot_base + (uint32_t)(q * 1024), voff[i]);
   };
 
-  f32x16 acc[4][TJ];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < TJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  f32x4 acc[FI][TJ];
 
-  const int l32 = lane & 31, lh = lane >> 5;
+  const int l16 = lane & 15, lg = lane >> 4;
   bf16x8 fr0[NF], fr1[NF];
-  // fragment f of k-step ks, in the order the MFMAs first use them:
-  // A0, B0 .. B(TJ-1), A1, A2, A3 (MFMAs run (i, j) i-major)
-  auto frag_addr = [&](int f, int ks) {
-    const int c = 2 * ks + lh;
-    if (f == 0) return C::swz(wn * 128 + l32, c);
-    if (f <= TJ) return C::swz(C::BN + wm * C::TW + 32 * (f - 1) + l32, c);
-    return C::swz(wn * 128 + 32 * (f - TJ) + l32, c);
+  // fragment f of a stage, in the order the MFMAs first use them:
+  // A0, B0 .. B(TJ-1), A1 .. A7 (MFMAs run (i, j) i-major)
+  auto frag_addr = [&](int f) {
+    if (f == 0) return C::swz(wn * 128 + l16, lg);
+    if (f <= TJ) return C::swz(C::BN + wm * C::TW + 16 * (f - 1) + l16, lg);
+    return C::swz(wn * 128 + 16 * (f - TJ) + l16, lg);
   };
   auto fa = [](bf16x8 (&f)[NF], int i) -> bf16x8& { return i == 0 ? f[0] : f[TJ + i]; };
   auto fb = [](bf16x8 (&f)[NF], int j) -> bf16x8& { return f[1 + j]; };
-  auto kstep = [&](bf16x8 (&cur)[NF], bf16x8 (&nxt)[NF], const u32x4* L, int nks, bool with_dma, const i32x4& rW,
-                   const i32x4& rX, uint32_t dma_base) {
+  constexpr int RPS = (NF + NSL - 1) / NSL;  // fragment reads per slice
+  auto kstep = [&](bf16x8 (&cur)[NF], bf16x8 (&nxt)[NF], const u32x4* L, const i32x4& rW, const i32x4& rX,
+                   uint32_t dma_base, auto first_) {
 #pragma unroll
     for (int r = 0; r < NSL; ++r) {
-      const int i = r / (TJ / 2), j0 = 2 * (r % (TJ / 2));
-      acc[i][j0] = mfma32_chunk(acc[i][j0], fa(cur, i), fb(cur, j0));
-      acc[i][j0 + 1] = mfma32_chunk(acc[i][j0 + 1], fa(cur, i), fb(cur, j0 + 1));
+      const int i = r / (TJ / 4), j0 = 4 * (r % (TJ / 4));
 #pragma unroll
-      for (int f = r; f < NF; f += NSL) nxt[f] = __builtin_bit_cast(bf16x8, L[frag_addr(f, nks)]);
-      if (with_dma) {
+      for (int u = 0; u < 4; ++u)
+        acc[i][j0 + u] = mfma16_chunk(decltype(first_)::value ? f32x4{0.f, 0.f, 0.f, 0.f} : acc[i][j0 + u], fa(cur, i),
+                                      fb(cur, j0 + u));
 #pragma unroll
-        for (int u = r; u < C::PER; u += NSL) dma(u, rW, rX, dma_base);
-      }
+      for (int f = r * RPS; f < (r + 1) * RPS && f < NF; ++f) nxt[f] = __builtin_bit_cast(bf16x8, L[frag_addr(f)]);
+#pragma unroll
+      for (int u = r; u < C::PER; u += NSL) dma(u, rW, rX, dma_base);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  const i32x4 none{0, 0, 0, 0};
-  auto stage = [&](int kt, auto s_) {
-    constexpr int S = decltype(s_)::value % NS;
-    const u32x4* cur = ring + S * C::SLOT;
-#pragma unroll
-    for (int ks = 0; ks + 1 < C::KS; ++ks) {
-      if (ks % 2 == 0) kstep(fr0, fr1, cur, ks + 1, false, none, none, 0);
-      else kstep(fr1, fr0, cur, ks + 1, false, none, none, 0);
-    }
+  auto stage = [&](int kt, bf16x8 (&cur)[NF], bf16x8 (&nxt)[NF], auto first_) {
+    const int S = kt & (NS - 1);
     // stage kt+1 has landed once at most this wave's DMAs of stage kt+2 are
     // outstanding; after the barrier that holds for every wave, and every
     // wave has finished stage kt-1 (its fragment reads completed before its
-    // MFMAs ran), so that slot takes stage kt+NS-1.  The reads of stage kt
-    // still in flight need no wait: nothing overwrites its slot now.
+    // MFMAs ran), so that slot takes stage kt+NS-1.
     wait_vmcnt<(NS - 3) * C::PER>();
     barrier_only();
-    const u32x4* nxt = ring + ((S + 1) % NS) * C::SLOT;
-    kstep(fr1, fr0, nxt, 0, true, rsrc_w(kt + NS - 1), rsrc_x(kt + NS - 1),
-          ring_base + (uint32_t)(((S + NS - 1) % NS) * C::SLOT * 16));
+    kstep(cur, nxt, ring + ((S + 1) % NS) * C::SLOT, rsrc_w(kt + NS - 1), rsrc_x(kt + NS - 1),
+          ring_base + (uint32_t)(((S + NS - 1) % NS) * C::SLOT * 16), first_);
   };
 
 #pragma unroll
@@ -512,23 +502,20 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
   wait_vmcnt<(NS - 2) * C::PER>();
   lds_barrier();
 #pragma unroll
-  for (int f = 0; f < NF; ++f) fr0[f] = __builtin_bit_cast(bf16x8, ring[frag_addr(f, 0)]);
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
-  int kt = 0;
+  for (int f = 0; f < NF; ++f) fr0[f] = __builtin_bit_cast(bf16x8, ring[frag_addr(f)]);
+  using Yes = std::true_type;
+  using No = std::false_type;
   static_assert(NS == 4, "ring of four slots");
-  for (; kt + 4 <= nk; kt += 4) {
-    stage(kt, I0{});
-    stage(kt + 1, I1{});
-    stage(kt + 2, I2{});
-    stage(kt + 3, I3{});
+  // The first stage starts every accumulator from zero inside its MFMAs, so
+  // the loop begins with distinct values (accumulators set to one shared zero
+  // beforehand make the register allocator shuffle them on every trip).
+  stage(0, fr0, fr1, Yes{});
+  int kt = 1;
+  for (; kt + 2 <= nk; kt += 2) {
+    stage(kt, fr1, fr0, No{});
+    stage(kt + 1, fr0, fr1, No{});
   }
-  if (kt < nk) {  // nk is even: at most two stages remain (slots 0, 1)
-    stage(kt, I0{});
-    stage(kt + 1, I1{});
-  }
+  stage(kt, fr1, fr0, No{});  // nk is even: one stage remains
   wait_vmcnt<0>();
 
   if constexpr (EPI == (int)Epi::SWIGLU) {
@@ -542,18 +529,16 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
     __syncthreads();  // every wave is done with the ring
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const int tl = wm * C::TW + 32 * j + l32;
+      const int tl = wm * C::TW + 16 * j + l16;
       const float r = m0 + tl < a.M ? a.rowscale[m0 + tl] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int cl = wn * 64 + 16 * i + 4 * g + 2 * lh;  // s column inside the tile (even)
-          const float v0 = acc[i][j][4 * g] * r, v1 = acc[i][j][4 * g + 1] * r;
-          const float v2 = acc[i][j][4 * g + 2] * r, v3 = acc[i][j][4 * g + 3] * r;
-          *reinterpret_cast<bf16x2*>(st + ((cl >> 5) * C::BM + tl) * RS + (cl & 31)) =
-              bf16x2{from_f32<bf16>(silu(v0) * v1), from_f32<bf16>(silu(v2) * v3)};
-        }
+      for (int i = 0; i < FI; ++i) {
+        const int cl = wn * 64 + 8 * i + 2 * lg;  // s column inside the tile (even)
+        const float v0 = acc[i][j][0] * r, v1 = acc[i][j][1] * r;
+        const float v2 = acc[i][j][2] * r, v3 = acc[i][j][3] * r;
+        *reinterpret_cast<bf16x2*>(st + ((cl >> 5) * C::BM + tl) * RS + (cl & 31)) =
+            bf16x2{from_f32<bf16>(silu(v0) * v1), from_f32<bf16>(silu(v2) * v3)};
+      }
     }
     __syncthreads();
     // m0 may be the second half of a 256-row tile (BM 128): tiled_off places
@@ -595,19 +580,16 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
         float rsj[TJ];
 #pragma unroll
         for (int j = 0; j < TJ; ++j) {
-          const int t = m0 + hh * 128 + C::pass_row(wm, hh) + 32 * j + l32;
+          const int t = m0 + hh * 128 + C::pass_row(wm, hh) + 16 * j + l16;
           rsj[j] = t < a.M ? a.rowscale[t] : 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FI; ++i)
 #pragma unroll
-          for (int j = 0; j < TJ; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int r = C::pass_row(wm, hh) + 32 * j + l32, c = (wn * 128 + 32 * i + 8 * g + 4 * lh) >> 2;
-              st[r * 64 + (c ^ (r & 63))] =
-                  f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]} * rsj[j];
-            }
+          for (int j = 0; j < TJ; ++j) {
+            const int r = C::pass_row(wm, hh) + 16 * j + l16, c = (wn * 128 + 16 * i + 4 * lg) >> 2;
+            st[r * 64 + (c ^ (r & 63))] = acc[i][j] * rsj[j];
+          }
       }
       if (has_v && tid < 8) {
         const int t0 = m0 + hh * 128 + 16 * tid;
@@ -783,15 +765,12 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
       }
       if (C::in_pass(wm, hh)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FI; ++i)
 #pragma unroll
-          for (int j = 0; j < TJ; ++j)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int r = C::pass_row(wm, hh) + 32 * j + l32, c = (wn * 128 + 32 * i + 8 * g + 4 * lh) >> 2;
-              st[r * 64 + (c ^ (r & 63))] =
-                  f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-            }
+          for (int j = 0; j < TJ; ++j) {
+            const int r = C::pass_row(wm, hh) + 16 * j + l16, c = (wn * 128 + 16 * i + 4 * lg) >> 2;
+            st[r * 64 + (c ^ (r & 63))] = acc[i][j];
+          }
       }
       __syncthreads();
       // A half whose 128 rows all lie before M takes a copy without the
@@ -850,17 +829,11 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
-      const int t = m0 + wm * C::TW + 32 * j + l32;
-      if (t < a.M) {
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int f = n0 + wn * 128 + 32 * i + 8 * g + 4 * lh;
-          epilogue<T, EPI>(a, t, f, f32x4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]});
-        }
-      }
+      const int t = m0 + wm * C::TW + 16 * j + l16;
+      if (t < a.M) epilogue<T, EPI>(a, t, n0 + wn * 128 + 16 * i + 4 * lg, acc[i][j]);
     }
 }
 
