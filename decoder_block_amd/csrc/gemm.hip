@@ -382,9 +382,14 @@ struct BigCfg {
   static constexpr int LDS_CHUNKS = NS * SLOT > 128 * 64 ? NS * SLOT : 128 * 64;
   static_assert(BM == 256 || BM == 128, "256 or 128 tokens per tile");
   static_assert(TJ % 4 == 0, "a slice is four MFMAs of one W fragment");
-  // 16 consecutive rows read one chunk each: the XOR spreads them over all
-  // 16-byte positions of a 256-byte bank window
-  static DEVI int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+  // Chunk position of logical chunk c in row r (rows are 64 bytes, four to a
+  // 256-byte bank window).  A fragment read has lane l on row 16k + (l & 15),
+  // chunk l >> 4, and a ds_read_b128 serves 16 lanes per cycle: those with
+  // equal bit 5 and equal parity of bits 2, 3, 4 (measured on this part).
+  // Flipping the chunk's high bit with row bit 2 gives those 16 lanes 16
+  // distinct 16-byte positions; the XOR with row bits 2-3 that suits 32
+  // rows per chunk (lanes 0-31 on one chunk) puts pairs of them on one.
+  static DEVI int swz(int r, int c) { return r * 4 + (c ^ (((r >> 2) & 1) << 1)); }
   // the staged epilogues handle 128 tokens at a time: wave row wm writes its
   // accumulators in pass hh when its tokens fall in that pass
   static DEVI bool in_pass(int wm, int hh) { return (wm * TW) / 128 == hh; }
