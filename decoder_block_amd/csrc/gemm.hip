@@ -524,38 +524,39 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs a) {
   wait_vmcnt<0>();
 
   if constexpr (EPI == (int)Epi::SWIGLU) {
-    // The tile's s = SiLU(r g) * (r u) is 256 tokens x 128 columns, i.e. the
-    // four 16 KB tiles (one row block, four column blocks) of the down GEMM's
-    // operand.  It is assembled in LDS (the ring is free now) and written out
-    // as contiguous 16-byte stores, instead of 4-byte pieces scattered over
-    // 32 rows per store instruction.
-    constexpr int RS = 40;  // LDS row pitch in elements: 80 bytes keeps 16-byte alignment, 2-way write conflicts
-    bf16* st = reinterpret_cast<bf16*>(ring);
-    __syncthreads();  // every wave is done with the ring
+    // The tile's s = SiLU(r g) * (r u) is BM tokens x 128 columns of the down
+    // GEMM's tiled operand (rows of a 32-column block 64 bytes apart).  In
+    // block (i, j) lane l holds columns 8i + 2(l >> 4) + {0, 1} of token
+    // 16j + (l & 15).  A 4 x 4 transpose across the wave's four 16-lane rows
+    // (lane swaps at distance 32, then 16) over blocks i0 .. i0+3 leaves lane l
+    // with the 8 consecutive columns 8(i0 + (l >> 4)) + {0..7} of its token:
+    // one 16-byte store per lane, and 16 tokens x 64 bytes = 1 KB contiguous
+    // per store instruction, with no trip through LDS.
+    // m0 may be the second half of a 256-row tile (BM 128): tiled_off places
+    // the tile's first row.
+    bf16* ob = reinterpret_cast<bf16*>(a.out) + tiled_off(m0, n0 / 2, a.ldo);
 #pragma unroll
     for (int j = 0; j < TJ; ++j) {
       const int tl = wm * C::TW + 16 * j + l16;
-      const float r = m0 + tl < a.M ? a.rowscale[m0 + tl] : 0.f;
+      const bool live = m0 + tl < a.M;
+      const float r = live ? a.rowscale[m0 + tl] : 0.f;
 #pragma unroll
-      for (int i = 0; i < FI; ++i) {
-        const int cl = wn * 64 + 8 * i + 2 * lg;  // s column inside the tile (even)
-        const float v0 = acc[i][j][0] * r, v1 = acc[i][j][1] * r;
-        const float v2 = acc[i][j][2] * r, v3 = acc[i][j][3] * r;
-        *reinterpret_cast<bf16x2*>(st + ((cl >> 5) * C::BM + tl) * RS + (cl & 31)) =
-            bf16x2{from_f32<bf16>(silu(v0) * v1), from_f32<bf16>(silu(v2) * v3)};
+      for (int i0 = 0; i0 < FI; i0 += 4) {
+        unsigned w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 v = acc[i0 + u][j] * r;
+          w[u] = __builtin_bit_cast(unsigned, bf16x2{from_f32<bf16>(silu(v[0]) * v[1]), from_f32<bf16>(silu(v[2]) * v[3])});
+        }
+        const auto p02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+        const auto p13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+        const auto p01 = __builtin_amdgcn_permlane16_swap(p02[0], p13[0], false, false);
+        const auto p23 = __builtin_amdgcn_permlane16_swap(p02[1], p13[1], false, false);
+        const int cl = wn * 64 + 8 * (i0 + lg);  // first s column of this lane's 16 bytes
+        if (live)
+          *reinterpret_cast<u32x4*>(ob + (cl >> 5) * kTileElems + tl * 32 + (cl & 31)) =
+              u32x4{p01[0], p01[1], p23[0], p23[1]};
       }
-    }
-    __syncthreads();
-    // m0 may be the second half of a 256-row tile (BM 128): tiled_off places
-    // the tile's first row, and rows of one column block are 64 bytes apart
-    bf16* ob = reinterpret_cast<bf16*>(a.out) + tiled_off(m0, n0 / 2, a.ldo);
-#pragma unroll
-    for (int p = 0; p < C::BM / 16; ++p) {
-      const int idx = p * 256 + tid;  // 16-byte piece: column block, row, chunk
-      const int cb = idx / (C::BM * 4), row = (idx >> 2) % C::BM, ch = idx & 3;
-      if (m0 + row < a.M)
-        *reinterpret_cast<u32x4*>(ob + cb * kTileElems + row * 32 + ch * 8) =
-            *reinterpret_cast<const u32x4*>(st + (cb * C::BM + row) * RS + ch * 8);
     }
     return;
   }
