@@ -354,7 +354,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(GemmArgs a) {
 // fewer than two rounds of the 256 CUs (e.g. the 4096-feature projections of
 // a 2048-token prefill: 128 tiles).
 // K is staged 32 elements at a time (one 32-deep k-step) in a 4-slot LDS
-// ring.  A stage is BM/32 * 4 slices of four MFMAs; the slices also read the
+// ring.  A stage is BM/16 slices of four MFMAs; the slices also read the
 // next stage's fragments (in the order the MFMAs consume them) and issue the
 // DMAs of stage kt+3, so with a single wave per SIMD the matrix core does not
 // wait for LDS:
